@@ -1,0 +1,13 @@
+"""CPU oracle for row-wise top-k index selection (test infrastructure only).
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may import this package.  It shares no code with the HIP path.
+"""
+
+from .topk_oracle import (  # noqa: F401
+    check_row,
+    is_untied,
+    oracle_topk,
+    oracle_topk_row,
+    row_view,
+)
