@@ -1,0 +1,140 @@
+/*
+ * mi_topk — batched, row-wise, stride-correct top-k index selection over fp32
+ * logits, for gfx950 (MI355X).
+ *
+ * The operation.  For every row i of a batch of fp32 logits, return the column
+ * indices of the k largest values among the row's first L_i entries:
+ *
+ *   - Row i starts i * row_stride elements after `logits`.  row_stride is the
+ *     memory stride between rows (torch `stride(0)`), which may exceed the
+ *     logical width: the logits producer of the DeepSeek-V4 indexer pads its
+ *     max-model-len axis to a multiple of 256 and then slices it, and taking
+ *     the width as the stride selects from the wrong memory (vLLM PR #42169
+ *     report, "Implementation breakdown" and the csrc/topk.cu excerpt).
+ *   - Only entries [0, L_i) of a row are candidates; entries [L_i, row_stride)
+ *     are never selected and their contents are irrelevant (SGLang PR #34167
+ *     page, TopKCluster::forward excerpt: the scan covers problem.seq_len).
+ *   - m_i = min(k, L_i) indices are returned.  Every entry strictly above the
+ *     m_i-th largest value v* is included; the remaining slots are taken from
+ *     the entries equal to v*, lowest index first (same excerpt: values at or
+ *     above the upper bucket bound are always emitted, the threshold bucket is
+ *     resolved separately).  Values are compared in IEEE order: -0.0 equals
+ *     +0.0 and -inf is an ordinary value.  NaN inside [0, L_i) is outside the
+ *     contract: the output is then still m_i distinct indices in [0, L_i).
+ *   - Output row i holds the m_i selected indices in ascending order in slots
+ *     [0, m_i) and -1 in slots [m_i, k).  Every slot is written.
+ *
+ * Memory and ownership.  The caller owns every buffer; the library never
+ * allocates, frees or synchronises on the call path, and enqueues all work on
+ * `stream`.  All pointers passed to topk_indices are device pointers.
+ *
+ * Workspace.  topk_workspace_size() gives the bytes of device workspace a call
+ * needs (0 for batches that one workgroup per row handles).  The workspace
+ * must be zero-filled before its first use.  Its counters and histograms are
+ * returned to zero by the kernels of every call that returns MI_TOPK_OK (the
+ * rest of it is scratch), so one buffer can be reused by consecutive calls on
+ * one stream without clearing it again.  Calls that run concurrently
+ * (different streams) must use different workspaces.
+ * The first 4 bytes of the workspace are a sticky error word: nonzero after a
+ * kernel gave up waiting at a cross-workgroup barrier (that call's output is
+ * then invalid and the workspace must be zero-filled again).
+ */
+#ifndef MI_TOPK_H
+#define MI_TOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MI_TOPK_OK 0
+#define MI_TOPK_EINVAL 1     /* bad argument; nothing was launched, out untouched */
+#define MI_TOPK_EWORKSPACE 2 /* workspace_bytes below topk_workspace_size()       */
+#define MI_TOPK_ELAUNCH 3    /* a HIP call failed (launch or device query)         */
+#define MI_TOPK_ETOOLONG 4   /* rows too long to keep on chip across the device    */
+
+/* Largest k accepted. */
+#define MI_TOPK_MAX_K (1 << 24)
+
+/*
+ * Bytes of device workspace topk_indices() needs for this batch shape on the
+ * current HIP device, for any alignment of `logits`.  Returns 0 when no
+ * workspace is needed, and also for arguments topk_indices() would reject.
+ */
+size_t topk_workspace_size(int64_t num_rows, int64_t row_stride, int32_t k);
+
+/*
+ * Row-wise top-k index selection (the operation described above).
+ *
+ *   logits      device fp32, at least (num_rows-1)*row_stride + max L_i
+ *               elements, 4-byte aligned (any 16-byte misalignment is fine).
+ *   row_stride  elements between the starts of consecutive rows, >= 1.
+ *   lengths     device int32 [num_rows]: L_i.  Values are clamped into
+ *               [0, row_stride] on the device; the host never reads them.
+ *   num_rows    rows in the batch, 0 <= num_rows <= INT32_MAX; 0 is a no-op.
+ *   k           1 <= k <= MI_TOPK_MAX_K.
+ *   out         device int32 [num_rows, k], contiguous (row stride k).
+ *   workspace   device buffer of workspace_bytes, zero-filled before first use
+ *               (see above); may be NULL when topk_workspace_size() is 0.
+ *   stream      HIP stream the kernels are enqueued on.
+ *
+ * Returns MI_TOPK_OK, or a status code above.  On MI_TOPK_EINVAL,
+ * MI_TOPK_EWORKSPACE and MI_TOPK_ETOOLONG nothing is enqueued.
+ */
+int topk_indices(const float* logits, int64_t row_stride, const int32_t* lengths,
+                 int64_t num_rows, int32_t k, int32_t* out, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* topk_status_string(int status);
+
+/*
+ * Path control, for cross-checking the kernels' paths against each other on
+ * the same input.  `path`:
+ *   MI_TOPK_PATH_AUTO   the choice topk_indices() makes;
+ *   MI_TOPK_PATH_LOCAL  one workgroup per row holds the whole row on chip
+ *                       (rows up to 32768 entries);
+ *   MI_TOPK_PATH_SPLIT  `chunks` workgroups per row (0 = automatic) hold one
+ *                       chunk each and merge their histograms in workspace.
+ * topk_workspace_size_path() and topk_indices_path() otherwise behave like
+ * topk_workspace_size() and topk_indices().
+ */
+#define MI_TOPK_PATH_AUTO 0
+#define MI_TOPK_PATH_LOCAL 1
+#define MI_TOPK_PATH_SPLIT 2
+
+size_t topk_workspace_size_path(int64_t num_rows, int64_t row_stride, int32_t k,
+                                int32_t path, int32_t chunks);
+
+int topk_indices_path(const float* logits, int64_t row_stride, const int32_t* lengths,
+                      int64_t num_rows, int32_t k, int32_t* out, void* workspace,
+                      size_t workspace_bytes, int32_t path, int32_t chunks,
+                      hipStream_t stream);
+
+/*
+ * Describe the launch topk_indices_path() would make, without launching:
+ * writes up to 7 int64 values to `info` (path, block threads, elements per
+ * thread, chunk elements, chunks per row, grid workgroups, workspace bytes)
+ * for a 16-byte-aligned `logits`.  Returns a status code.
+ */
+int topk_plan_describe(int64_t num_rows, int64_t row_stride, int32_t k, int32_t path,
+                       int32_t chunks, int64_t* info);
+
+/*
+ * Diagnostic: the order-preserving key the kernels give each fp32 value
+ * (x < y implies key(x) < key(y); -0.0 and +0.0 share a key; every value,
+ * NaN included, maps to a key >= 1).  in and out are device arrays of n
+ * elements.  Returns a status code.
+ */
+int topk_debug_keys(const float* in, uint32_t* out, int64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI_TOPK_H */

@@ -1,0 +1,171 @@
+"""Python binding of ``libmi_topk.so``: row-wise top-k index selection on gfx950.
+
+Argument marshalling only: every step of the selection runs in the library's
+HIP kernels.  PyTorch provides device memory and the stream.  The functions
+raise if the library has not been built (``python -m row_wise_top_topk_amd.build``);
+there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "PATH_AUTO", "PATH_LOCAL", "PATH_SPLIT",
+    "library_path", "load_library", "topk_indices", "workspace_size",
+    "plan_describe", "debug_keys", "workspace_error", "status_string",
+]
+
+PATH_AUTO, PATH_LOCAL, PATH_SPLIT = 0, 1, 2
+_PATHS = {"auto": PATH_AUTO, "local": PATH_LOCAL, "split": PATH_SPLIT}
+MAX_K = 1 << 24
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+_lib_lock = threading.Lock()
+_ws_cache: dict = {}
+
+
+def library_path() -> str:
+    return os.environ.get("MI_TOPK_LIB", os.path.join(_HERE, "libmi_topk.so"))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libmi_topk.so once; raise if it is missing."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m row_wise_top_topk_amd.build`")
+        lib = ctypes.CDLL(path)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+        lib.topk_workspace_size.argtypes = [i64, i64, i32]
+        lib.topk_workspace_size.restype = sz
+        lib.topk_workspace_size_path.argtypes = [i64, i64, i32, i32, i32]
+        lib.topk_workspace_size_path.restype = sz
+        lib.topk_indices.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, vp]
+        lib.topk_indices.restype = ctypes.c_int
+        lib.topk_indices_path.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, i32, i32, vp]
+        lib.topk_indices_path.restype = ctypes.c_int
+        lib.topk_plan_describe.argtypes = [i64, i64, i32, i32, i32, ctypes.POINTER(i64)]
+        lib.topk_plan_describe.restype = ctypes.c_int
+        lib.topk_status_string.argtypes = [ctypes.c_int]
+        lib.topk_status_string.restype = ctypes.c_char_p
+        lib.topk_debug_keys.argtypes = [vp, vp, i64, vp]
+        lib.topk_debug_keys.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().topk_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise RuntimeError(f"{what} failed: {status_string(status)} (status {status})")
+
+
+def _path_id(path) -> int:
+    if isinstance(path, str):
+        return _PATHS[path]
+    return int(path)
+
+
+def workspace_size(num_rows: int, row_stride: int, k: int, path="auto", chunks: int = 0) -> int:
+    """Bytes of zero-filled device workspace a call with this shape needs."""
+    return int(load_library().topk_workspace_size_path(
+        int(num_rows), int(row_stride), int(k), _path_id(path), int(chunks)))
+
+
+def plan_describe(num_rows: int, row_stride: int, k: int, path="auto", chunks: int = 0) -> dict:
+    """The launch the library makes for this shape (16-byte-aligned logits)."""
+    info = (ctypes.c_int64 * 7)()
+    _check(load_library().topk_plan_describe(int(num_rows), int(row_stride), int(k),
+                                             _path_id(path), int(chunks), info), "topk_plan_describe")
+    keys = ("path", "block", "elems_per_thread", "chunk", "chunks_per_row", "grid", "workspace_bytes")
+    return dict(zip(keys, (int(v) for v in info)))
+
+
+def _cached_workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+    key = (device.index, stream)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def topk_indices(logits: torch.Tensor, lengths: torch.Tensor, k: int, out: torch.Tensor = None,
+                 workspace: torch.Tensor = None, path="auto", chunks: int = 0) -> torch.Tensor:
+    """Indices of the k largest of ``logits[i, :lengths[i]]`` for every row i.
+
+    ``logits``: float32 device tensor, 2-D, ``stride(1) == 1``; ``stride(0)``
+    is passed as the row stride (it may exceed the width).  ``lengths``: int32
+    device tensor ``[rows]``.  Returns int32 ``[rows, k]``: selected indices in
+    ascending order, then -1.  ``workspace`` (uint8, zero-filled before first
+    use) is allocated and cached per stream when not given.
+    """
+    lib = load_library()
+    if not isinstance(logits, torch.Tensor) or logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be a 2-D float32 tensor")
+    if not logits.is_cuda:
+        raise ValueError("logits must be on a GPU")
+    if logits.shape[0] > 0 and logits.shape[1] > 1 and logits.stride(1) != 1:
+        raise ValueError("logits must have unit stride along its last axis")
+    if lengths.dtype != torch.int32 or lengths.dim() != 1 or lengths.device != logits.device:
+        raise ValueError("lengths must be a 1-D int32 tensor on the logits' device")
+    if not lengths.is_contiguous():
+        raise ValueError("lengths must be contiguous")
+    rows = int(logits.shape[0])
+    if lengths.shape[0] != rows:
+        raise ValueError("lengths must have one entry per row")
+    k = int(k)
+    if not 1 <= k <= MAX_K:
+        raise ValueError(f"k must be in [1, {MAX_K}]")
+    row_stride = int(logits.stride(0)) if rows > 1 else max(int(logits.stride(0)), int(logits.shape[1]), 1)
+    device = logits.device
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=device)
+    elif (out.dtype != torch.int32 or tuple(out.shape) != (rows, k) or not out.is_contiguous()
+          or out.device != device):
+        raise ValueError("out must be a contiguous int32 [rows, k] tensor on the logits' device")
+    if rows == 0:
+        return out
+    pid = _path_id(path)
+    stream = torch.cuda.current_stream(device).cuda_stream
+    need = int(lib.topk_workspace_size_path(rows, row_stride, k, pid, int(chunks)))
+    ws_ptr, ws_bytes = None, 0
+    if need > 0:
+        if workspace is None:
+            workspace = _cached_workspace(device, stream, need)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(device):
+        st = lib.topk_indices_path(logits.data_ptr(), row_stride, lengths.data_ptr(), rows, k,
+                                   out.data_ptr(), ws_ptr, ws_bytes, pid, int(chunks), stream)
+    _check(st, "topk_indices")
+    return out
+
+
+def workspace_error(workspace: torch.Tensor) -> int:
+    """The sticky error word of a workspace (nonzero: a barrier wait gave up)."""
+    return int(workspace[:4].view(torch.int32).item())
+
+
+def debug_keys(x: torch.Tensor) -> torch.Tensor:
+    """The kernels' order-preserving uint32 key of each float32 value (as int32 bits)."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 GPU tensor")
+    out = torch.empty(x.shape, dtype=torch.int32, device=x.device)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        _check(load_library().topk_debug_keys(x.data_ptr(), out.data_ptr(), x.numel(), stream),
+               "topk_debug_keys")
+    return out

@@ -1,0 +1,783 @@
+// Row-wise top-k index selection kernels for gfx950 (MI355X) and the C ABI
+// that launches them.
+//
+// Paths (chosen on the host from num_rows, row_stride and k; each row then
+// branches on its own length on the device):
+//   * trivial  — L_i <= k: every index 0..L_i-1, then -1.  No logits are read.
+//   * local    — one workgroup per row.  The row is read from HBM once, with
+//                16-byte loads, into registers as order-preserving keys; all
+//                radix rounds then run on-chip (LDS histograms), and the
+//                selected indices are written in ascending order.
+//   * split    — for long rows, or too few rows to fill the device: G
+//                workgroups per row each hold one chunk in registers, merge
+//                their digit histograms into a per-row workspace histogram
+//                with device-scope atomics, and meet at a per-row barrier.
+//                Once the threshold bucket is small enough its entries are
+//                gathered into a candidate list that every workgroup of the
+//                row finishes on-chip, so a row needs two barriers in the
+//                common case.  All workgroups of a launch are co-resident
+//                (cooperative launch), so the barrier waits always end.
+// The intra-row split over an 8-CTA cluster with DSMEM on the SGLang
+// PR #34167 page (TopKCluster::forward) is prior art for the split path; here
+// the merge goes through global atomics because CDNA has no clusters.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "mi_topk.h"
+#include "select_device.hpp"
+#include "wave64.hpp"
+
+#define MI_TOPK_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace mitopk {
+namespace {
+
+constexpr int kCandCap = 4096;     // candidate list entries (split path)
+constexpr int kMaxChunks = 1024;   // workgroups per row (split path)
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+struct Params {
+  const float* logits;
+  int64_t row_stride;
+  const int32_t* lengths;
+  int64_t num_rows;
+  int32_t* out;
+  uint8_t* ws;
+  int32_t k;
+  int32_t chunk;          // split: elements per chunk, a multiple of 4
+  int32_t G;              // split: workgroups per row
+  int32_t rows_per_iter;  // split: rows processed per pass of the grid
+};
+
+// Per-row workspace of the split path.  Every field starts at zero and is
+// returned to zero by the last workgroup to leave the row.
+struct RowWs {
+  uint32_t bar;         // arrivals at the row's barriers
+  uint32_t cand_count;  // candidate list fill
+  uint32_t pad[62];
+  uint32_t hist[kFirstBins + (kMaxRounds - 1) * kNextBins];  // one histogram per round
+  uint32_t wg_count[kMaxChunks];                             // published per-workgroup counts
+  uint64_t cand[kCandCap];                                   // (key << 32) | column
+};
+constexpr size_t kWsHeader = 256;  // word 0: sticky error flag
+static_assert(sizeof(RowWs) % 256 == 0, "row workspace keeps 256-byte alignment");
+
+__device__ __forceinline__ uint32_t hist_offset(int round) {
+  return round == 0 ? 0u : static_cast<uint32_t>(kFirstBins + (round - 1) * kNextBins);
+}
+
+// ---- device-scope memory helpers (coherent across the XCDs' L2 caches) ----
+__device__ __forceinline__ void g_add(uint32_t* p, uint32_t v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t g_load(uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void g_store(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t g_load64(uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void g_store64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Barrier among the `target / n_instance` workgroups of one row.  Every
+// thread releases its prior global writes at device scope; thread 0 arrives
+// and waits until `target` arrivals are counted.  The wait is bounded: after
+// kSpinLimit polls it sets the sticky error word and gives up, so a wave can
+// never wait forever.
+__device__ __forceinline__ void row_barrier(uint32_t* bar, uint32_t target, uint32_t* err) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t spins = 0;
+    while (__hip_atomic_load(bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins == kSpinLimit) {
+        g_store(err, 1u);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// A chunk of a row held in registers: NS = E/4 slots of 16 bytes per thread.
+// Slot s of thread t covers chunk elements 4q..4q+3 with q = s*BLOCK + t, so
+// each load instruction of a wavefront reads 1 KiB of consecutive memory.
+// Elements are addressed from the 16-byte-aligned address at or below the
+// row start; element e of the chunk is column jbase + e of the row.
+struct Chunk {
+  const float* base;  // 16-byte aligned
+  int llo, lhi;       // valid elements [llo, lhi) of the chunk (llo <= 3)
+  int hi_slot;        // slots [0, hi_slot) hold at least one valid element
+  int32_t jbase;
+};
+
+__device__ __forceinline__ Chunk make_chunk(const float* row_ptr, int head, int64_t cbase, int llo,
+                                            int lhi) {
+  Chunk ch;
+  ch.base = row_ptr - head + cbase;
+  ch.llo = llo;
+  ch.lhi = lhi;
+  ch.hi_slot = (lhi + 3) >> 2;
+  ch.jbase = static_cast<int32_t>(cbase - head);
+  return ch;
+}
+
+// Loads the chunk and converts it to keys.  All loads are issued before any
+// is consumed (no branch between them), through a buffer resource whose
+// bound is the end of the last slot holding a valid element: lanes past it
+// read zeros without touching memory.  Entries outside [llo, lhi) are then set to key 0;
+// that test is uniform for every slot row except the one or two that hold
+// the row's start or end.
+template <int BLOCK, int E>
+__device__ __forceinline__ void load_keys(uint32_t (&key)[E], const Chunk& ch) {
+  constexpr int NS = E / 4;
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(ch.base), 0, ch.hi_slot * 16, 0x00020000);
+  using u32x4 = __attribute__((ext_vector_type(4))) uint32_t;
+  u32x4 raw[NS];
+  // The whole byte offset goes in the vector offset: that is the part the
+  // hardware range-checks against the resource's size (the scalar offset is
+  // not checked), so slots past the bound are never read.
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    raw[s] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (s * BLOCK + tid) * 16, 0, 0);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) key[4 * s + c] = order_key_bits(raw[s][c]);
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int e_first = s * BLOCK * 4;
+    if (e_first >= ch.lhi) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) key[4 * s + c] = 0u;
+    } else if (e_first + BLOCK * 4 > ch.lhi || e_first < ch.llo) {
+      const int e0 = 4 * (s * BLOCK + tid);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool ok = e0 + c >= ch.llo && e0 + c < ch.lhi;
+        key[4 * s + c] = ok ? key[4 * s + c] : 0u;
+      }
+    }
+  }
+}
+
+// The register-held chunk as a source of (key, column) entries.  Slots with
+// no valid element hold key 0, which no prefix test accepts, so the generic
+// passes visit every slot without a bounds test.  The column base goes
+// through an empty asm statement so that the compiler derives the columns
+// afresh at each use instead of keeping one register per element alive
+// across the radix rounds.
+template <int BLOCK, int E>
+struct RegSource {
+  const uint32_t (&key)[E];
+  const Chunk& ch;
+
+  template <class F>
+  __device__ __forceinline__ void operator()(F f) const {
+    constexpr int NS = E / 4;
+    int32_t jt = ch.jbase + 4 * static_cast<int32_t>(threadIdx.x);
+    asm volatile("" : "+v"(jt));
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) f(key[4 * s + c], jt + 4 * s * BLOCK + c);
+    }
+  }
+
+  // Histogram of digit d below prefix p.  For the first digit every loaded
+  // slot is counted without a per-entry test; the few entries outside the
+  // row in the first and last slot (key 0, bin 0) are subtracted again.
+  __device__ __forceinline__ void count(const Prefix& p, int d, int ib, uint32_t rmask,
+                                        uint32_t* hist) const {
+    if (p.bits != 0) {
+      count_digit(*this, p, d, ib, rmask, hist);
+      return;
+    }
+    constexpr int NS = E / 4;
+    const int sh = 32 - d;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int e_first = s * BLOCK * 4;
+      if (e_first + BLOCK * 4 <= ch.lhi) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) atomicAdd(&hist[key[4 * s + c] >> sh], 1u);
+      } else if (e_first < ch.lhi) {
+        if (s * BLOCK + tid < ch.hi_slot) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) atomicAdd(&hist[key[4 * s + c] >> sh], 1u);
+        }
+      }
+    }
+    if (tid == 0) atomicSub(&hist[0], static_cast<uint32_t>(4 * ch.hi_slot - (ch.lhi - ch.llo)));
+  }
+};
+
+// The n entries of an LDS candidate list, visited thread-strided.
+template <int BLOCK>
+struct ListSource {
+  const uint64_t* list;
+  int n;
+  template <class F>
+  __device__ __forceinline__ void operator()(F f) const {
+    for (int i = threadIdx.x; i < n; i += BLOCK) {
+      const uint64_t e = list[i];
+      f(static_cast<uint32_t>(e >> 32), static_cast<int32_t>(static_cast<uint32_t>(e)));
+    }
+  }
+  __device__ __forceinline__ void count(const Prefix& p, int d, int ib, uint32_t rmask,
+                                        uint32_t* hist) const {
+    count_digit(*this, p, d, ib, rmask, hist);
+  }
+};
+
+// Writes the chunk's selected elements (composite prefix >= p) to
+// out_row[base ...] in ascending column order.  The per-slot counts of a
+// thread (at most 4 each) are packed two to a word in 16-bit fields, so one
+// workgroup prefix sum gives every slot of every thread its output position
+// (slot-major, then thread, then lane is column order).
+template <int BLOCK, int E, class Pred>
+__device__ __forceinline__ void emit_ordered_pred(const uint32_t (&key)[E], const Chunk& ch,
+                                                  const Pred& pred, int32_t* out_row, uint32_t base,
+                                                  uint32_t limit, uint32_t* lds_scan) {
+  constexpr int NS = E / 4;
+  constexpr int NP = (NS + 1) / 2;
+  const int tid = threadIdx.x;
+  int32_t jt = ch.jbase + 4 * tid;
+  asm volatile("" : "+v"(jt));
+  uint32_t packed[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) packed[i] = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (pred.ge(key[4 * s + c], jt + 4 * s * BLOCK + c)) packed[s >> 1] += 1u << ((s & 1) * 16);
+    }
+  }
+  uint32_t incl[NP], tot[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) incl[i] = packed[i];
+  block_inclusive_sum<BLOCK, NP>(incl, tot, lds_scan);
+  asm volatile("" : "+v"(jt));
+  uint32_t run = base;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int sh = (s & 1) * 16;
+    uint32_t pos = run + (((incl[s >> 1] - packed[s >> 1]) >> sh) & 0xFFFFu);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int32_t j = jt + 4 * s * BLOCK + c;
+      if (pred.ge(key[4 * s + c], j)) {
+        if (pos < limit) out_row[pos] = j;
+        ++pos;
+      }
+    }
+    run += (tot[s >> 1] >> sh) & 0xFFFFu;
+  }
+}
+
+template <int BLOCK, int E>
+__device__ __forceinline__ void emit_ordered(const uint32_t (&key)[E], const Chunk& ch,
+                                             const Prefix& p, int ib, int32_t* out_row,
+                                             uint32_t base, uint32_t limit, uint32_t* lds_scan) {
+  const uint32_t rmask = (1u << ib) - 1u;
+  with_pred(p, ib, rmask, [&](const auto& pred) {
+    emit_ordered_pred<BLOCK, E>(key, ch, pred, out_row, base, limit, lds_scan);
+  });
+}
+
+__device__ __forceinline__ void write_trivial(int32_t* out_row, int L, int k, int nthreads) {
+  for (int t = threadIdx.x; t < k; t += nthreads) out_row[t] = t < L ? t : -1;
+}
+
+__device__ __forceinline__ int index_bits(int L) {
+  // bits needed for column indices 0..L-1 (L >= 2 here)
+  return 32 - __clz(static_cast<uint32_t>(L - 1));
+}
+
+__device__ __forceinline__ int row_length(const Params& p, int64_t row) {
+  const int64_t L = p.lengths[row];
+  return static_cast<int>(L < 0 ? 0 : (L > p.row_stride ? p.row_stride : L));
+}
+
+// One row (or one chunk that holds a whole row) entirely inside the workgroup.
+template <int BLOCK, int E>
+__device__ __forceinline__ void select_whole_row(const uint32_t (&key)[E], const Chunk& ch, int L,
+                                                 int k, int32_t* out_row, uint32_t* hist,
+                                                 uint32_t* lds_scan, uint32_t* res) {
+  const int ib = index_bits(L);
+  const uint32_t m = static_cast<uint32_t>(k);  // L > k here
+  const Prefix pf = rounds_local<BLOCK>(RegSource<BLOCK, E>{key, ch}, Prefix{0, 0u, 0u}, m, ib,
+                                        hist, lds_scan, res);
+  emit_ordered<BLOCK, E>(key, ch, pf, ib, out_row, 0u, m, lds_scan);
+}
+
+// ---------------------------------------------------------------------------
+// Local path: one workgroup per row, whole row in registers.
+// ---------------------------------------------------------------------------
+template <int BLOCK, int E>
+__global__ void __launch_bounds__(BLOCK) topk_local_kernel(Params p) {
+  __shared__ uint32_t hist[kFirstBins];
+  __shared__ uint32_t lds_scan[scan_lds_words<BLOCK, 8>()];
+  __shared__ uint32_t res[4];
+  const int64_t row = blockIdx.x;
+  const int L = row_length(p, row);
+  int32_t* out_row = p.out + row * static_cast<int64_t>(p.k);
+  if (L <= p.k) {
+    write_trivial(out_row, L, p.k, BLOCK);
+    return;
+  }
+  const float* row_ptr = p.logits + row * p.row_stride;
+  const int head = static_cast<int>((reinterpret_cast<uintptr_t>(row_ptr) >> 2) & 3u);
+  const Chunk ch = make_chunk(row_ptr, head, 0, head, head + L);
+  uint32_t key[E];
+  load_keys<BLOCK, E>(key, ch);
+  select_whole_row<BLOCK, E>(key, ch, L, p.k, out_row, hist, lds_scan, res);
+}
+
+// ---------------------------------------------------------------------------
+// Split path: G workgroups per row, merged through the row workspace.
+// ---------------------------------------------------------------------------
+
+// Sum over the workgroup of one value per thread (every thread gets it).
+template <int BLOCK>
+__device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* lds_scan) {
+  uint32_t v[1] = {x}, tot[1];
+  block_inclusive_sum<BLOCK, 1>(v, tot, lds_scan);
+  return tot[0];
+}
+
+template <int BLOCK, int E>
+__global__ void __launch_bounds__(BLOCK) topk_split_kernel(Params p) {
+  __shared__ uint32_t hist[kFirstBins];
+  __shared__ uint64_t cand[kCandCap];
+  __shared__ uint32_t csel[kMaxChunks];
+  __shared__ uint32_t lds_scan[scan_lds_words<BLOCK, 8>()];
+  __shared__ uint32_t res[4];
+  const int tid = threadIdx.x;
+  const int G = p.G;
+  uint32_t* err = reinterpret_cast<uint32_t*>(p.ws);
+  RowWs* ws_rows = reinterpret_cast<RowWs*>(p.ws + kWsHeader);
+
+  for (int64_t row0 = 0; row0 < p.num_rows; row0 += p.rows_per_iter) {
+    __syncthreads();  // LDS is reused from the previous row
+    const int64_t row = row0 + blockIdx.x / G;
+    if (row >= p.num_rows) break;
+    const int g = blockIdx.x % G;
+    const int L = row_length(p, row);
+    int32_t* out_row = p.out + row * static_cast<int64_t>(p.k);
+    if (L <= p.k) {
+      if (g == 0) write_trivial(out_row, L, p.k, BLOCK);
+      continue;
+    }
+    const float* row_ptr = p.logits + row * p.row_stride;
+    const int head = static_cast<int>((reinterpret_cast<uintptr_t>(row_ptr) >> 2) & 3u);
+    const int64_t span = static_cast<int64_t>(head) + L;
+    const int Gr = static_cast<int>((span + p.chunk - 1) / p.chunk);
+    if (g >= Gr) continue;
+    const int64_t cbase = static_cast<int64_t>(g) * p.chunk;
+    const Chunk ch = make_chunk(row_ptr, head, cbase, g == 0 ? head : 0,
+                                static_cast<int>(span - cbase < p.chunk ? span - cbase : p.chunk));
+    uint32_t key[E];
+    load_keys<BLOCK, E>(key, ch);
+    if (Gr == 1) {
+      select_whole_row<BLOCK, E>(key, ch, L, p.k, out_row, hist, lds_scan, res);
+      continue;
+    }
+
+    RowWs* ws = ws_rows + row;
+    const int ib = index_bits(L);
+    const uint32_t rmask = (1u << ib) - 1u;
+    const RegSource<BLOCK, E> regs{key, ch};
+    const uint32_t nwg = static_cast<uint32_t>(Gr);
+    uint32_t need = static_cast<uint32_t>(p.k);
+    Prefix pr{0, 0u, 0u};
+    uint32_t nbar = 0;
+    int round = 0;
+    bool use_cand = false;
+    uint32_t cnt = 0;
+    // Global rounds: histogram the chunk, merge, wait for the row, search.
+    for (; round < kMaxRounds; ++round) {
+      const int d = digit_bits(pr.bits, ib);
+      const int nb = 1 << d;
+      for (int i = tid; i < nb; i += BLOCK) hist[i] = 0;
+      __syncthreads();
+      regs.count(pr, d, ib, rmask, hist);
+      __syncthreads();
+      uint32_t* gh = ws->hist + hist_offset(round);
+      for (int i = tid; i < nb; i += BLOCK) {
+        const uint32_t h = hist[i];
+        if (h != 0) g_add(&gh[i], h);
+      }
+      row_barrier(&ws->bar, ++nbar * nwg, err);
+      for (int i = tid; i < nb; i += BLOCK) hist[i] = g_load(&gh[i]);
+      __syncthreads();
+      find_bucket<BLOCK>(hist, nb, need, lds_scan, res);
+      const uint32_t b = res[0], gt = res[1];
+      cnt = res[2];
+      need -= gt;
+      pr = extend(pr, d, b);
+      if (cnt == need) break;
+      if (cnt <= static_cast<uint32_t>(kCandCap)) {
+        use_cand = true;
+        break;
+      }
+    }
+    const int rounds_used = round + 1;
+
+    Prefix pf = pr;
+    uint32_t off = 0;
+    if (!use_cand) {
+      // The prefix alone decides the set; publish counts for the output offsets.
+      uint32_t n = 0;
+      with_pred(pf, ib, rmask, [&](const auto& pred) {
+        regs([&](uint32_t kk, int32_t j) { n += pred.ge(kk, j) ? 1u : 0u; });
+      });
+      const uint32_t total = block_sum<BLOCK>(n, lds_scan);
+      if (tid == 0) g_store(&ws->wg_count[g], total);
+      row_barrier(&ws->bar, ++nbar * nwg, err);
+      uint32_t part = 0;
+      for (int i = tid; i < g; i += BLOCK) part += g_load(&ws->wg_count[i]);
+      off = block_sum<BLOCK>(part, lds_scan);
+    } else {
+      // Entries above the bucket are taken; the bucket's entries go to the
+      // row's candidate list, which every workgroup then finishes locally.
+      uint32_t n_sel = 0, n_cand = 0;
+      with_pred(pr, ib, rmask, [&](const auto& pred) {
+        regs([&](uint32_t kk, int32_t j) {
+          n_sel += pred.ge(kk, j) ? 1u : 0u;
+          n_cand += pred.eq(kk, j) ? 1u : 0u;
+        });
+      });
+      uint32_t v[2] = {n_sel - n_cand, n_cand}, tot[2];
+      block_inclusive_sum<BLOCK, 2>(v, tot, lds_scan);
+      if (tid == 0) {
+        res[3] = tot[1] ? __hip_atomic_fetch_add(&ws->cand_count, tot[1], __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                        : 0u;
+        g_store(&ws->wg_count[g], tot[0]);
+      }
+      __syncthreads();
+      uint32_t pos = res[3] + v[1] - n_cand;
+      with_pred(pr, ib, rmask, [&](const auto& pred) {
+        regs([&](uint32_t kk, int32_t j) {
+          if (pred.eq(kk, j)) {
+            if (pos < static_cast<uint32_t>(kCandCap))
+              g_store64(&ws->cand[pos], (static_cast<uint64_t>(kk) << 32) | static_cast<uint32_t>(j));
+            ++pos;
+          }
+        });
+      });
+      row_barrier(&ws->bar, ++nbar * nwg, err);
+      const int nc = static_cast<int>(cnt);
+      for (int i = tid; i < nc; i += BLOCK) cand[i] = g_load64(&ws->cand[i]);
+      __syncthreads();
+      pf = rounds_local<BLOCK>(ListSource<BLOCK>{cand, nc}, pr, need, ib, hist, lds_scan, res);
+      for (int i = tid; i < Gr; i += BLOCK) csel[i] = 0;
+      __syncthreads();
+      with_pred(pf, ib, rmask, [&](const auto& pred) {
+        for (int i = tid; i < nc; i += BLOCK) {
+          const uint64_t e = cand[i];
+          const uint32_t kk = static_cast<uint32_t>(e >> 32);
+          const int32_t j = static_cast<int32_t>(static_cast<uint32_t>(e));
+          if (pred.ge(kk, j)) atomicAdd(&csel[(j + head) / p.chunk], 1u);
+        }
+      });
+      __syncthreads();
+      uint32_t part = 0;
+      for (int i = tid; i < g; i += BLOCK) part += g_load(&ws->wg_count[i]) + csel[i];
+      off = block_sum<BLOCK>(part, lds_scan);
+    }
+    emit_ordered<BLOCK, E>(key, ch, pf, ib, out_row, off, static_cast<uint32_t>(p.k), lds_scan);
+
+    // Leave the row; the last workgroup out returns its workspace to zero.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(&ws->bar, 1u, __ATOMIC_ACQ_REL,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      res[3] = old == (nbar + 1) * nwg - 1u ? 1u : 0u;
+    }
+    __syncthreads();
+    if (res[3]) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      for (int r = 0; r < rounds_used; ++r) {
+        const int nbins = r == 0 ? kFirstBins : kNextBins;
+        uint32_t* gh = ws->hist + hist_offset(r);
+        for (int i = tid; i < nbins; i += BLOCK) g_store(&gh[i], 0u);
+      }
+      if (tid == 0) g_store(&ws->cand_count, 0u);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();
+      if (tid == 0) g_store(&ws->bar, 0u);
+    }
+  }
+}
+
+__global__ void debug_keys_kernel(const float* in, uint32_t* out, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = order_key(in[i]);
+}
+
+// ---------------------------------------------------------------------------
+// Host side: planning and launch.
+// ---------------------------------------------------------------------------
+enum Kind { kLocal256x16, kLocal512x16, kLocal1024x16, kLocal1024x32, kSplit1024x16, kNumKinds };
+constexpr int kLargestLocal = kLocal1024x32;
+
+struct KindInfo {
+  int block, e;
+  bool split;
+  const void* fn;
+};
+
+const KindInfo kKinds[kNumKinds] = {
+    {256, 16, false, reinterpret_cast<const void*>(&topk_local_kernel<256, 16>)},
+    {512, 16, false, reinterpret_cast<const void*>(&topk_local_kernel<512, 16>)},
+    {1024, 16, false, reinterpret_cast<const void*>(&topk_local_kernel<1024, 16>)},
+    {1024, 32, false, reinterpret_cast<const void*>(&topk_local_kernel<1024, 32>)},
+    {1024, 16, true, reinterpret_cast<const void*>(&topk_split_kernel<1024, 16>)},
+};
+
+struct DeviceInfo {
+  int cus = 0;
+  int coop = 0;
+  int split_per_cu = 0;  // co-resident split workgroups per CU
+  hipError_t status = hipSuccess;
+};
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+DeviceInfo g_dev[kMaxDevices];
+
+hipError_t device_info(DeviceInfo* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_dev_once[dev], [dev]() {
+    DeviceInfo d;
+    d.status = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (d.status == hipSuccess)
+      d.status = hipDeviceGetAttribute(&d.coop, hipDeviceAttributeCooperativeLaunch, dev);
+    if (d.status == hipSuccess)
+      d.status = hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.split_per_cu, kKinds[kSplit1024x16].fn,
+                                                              kKinds[kSplit1024x16].block, 0);
+    g_dev[dev] = d;
+  });
+  *out = g_dev[dev];
+  return out->status;
+}
+
+struct Plan {
+  int kind = kLocal256x16;
+  int64_t chunk = 0;
+  int G = 1;
+  int rows_per_iter = 0;
+  int64_t grid = 0;
+  size_t ws_bytes = 0;
+};
+
+int64_t cap_of(int kind) { return static_cast<int64_t>(kKinds[kind].block) * kKinds[kind].e; }
+
+// head_max: largest misalignment (in elements) of a row start below a 16-byte
+// boundary: 0 when logits is 16-byte aligned and row_stride % 4 == 0, else 3.
+int make_plan(int64_t num_rows, int64_t row_stride, int32_t k, int path, int chunks, int head_max,
+              const DeviceInfo& dev, Plan* pl) {
+  (void)k;
+  const int64_t need = row_stride + head_max;  // elements a row can span from its aligned start
+  bool split;
+  if (path == MI_TOPK_PATH_LOCAL) {
+    if (need > cap_of(kLargestLocal)) return MI_TOPK_ETOOLONG;
+    split = false;
+  } else if (path == MI_TOPK_PATH_SPLIT) {
+    split = true;
+  } else {
+    // Few long rows cannot fill the device with one workgroup each.
+    split = need > cap_of(kLargestLocal) ||
+            (need > 8192 && num_rows < 2 * static_cast<int64_t>(dev.cus));
+  }
+  if (!split) {
+    int kind = kLocal256x16;
+    while (cap_of(kind) < need) ++kind;
+    pl->kind = kind;
+    pl->chunk = cap_of(kind);
+    pl->G = 1;
+    pl->grid = num_rows;
+    pl->rows_per_iter = static_cast<int>(num_rows);
+    pl->ws_bytes = 0;
+    return MI_TOPK_OK;
+  }
+  if (!dev.coop || dev.split_per_cu < 1) return MI_TOPK_ELAUNCH;
+  const int64_t cap = cap_of(kSplit1024x16);
+  const int64_t max_res = static_cast<int64_t>(dev.split_per_cu) * dev.cus;
+  const int64_t g_min = (need + cap - 1) / cap;
+  int64_t G;
+  if (chunks > 0) {
+    G = chunks;
+  } else {
+    const int64_t g_fill = (max_res + num_rows - 1) / num_rows;
+    const int64_t g_most = std::max<int64_t>(1, (need + 4095) / 4096);  // chunks of >= 4096
+    G = std::max(g_min, std::min(g_fill, g_most));
+  }
+  if (G < g_min) return MI_TOPK_EINVAL;
+  int64_t chunk = ((need + G - 1) / G + 3) & ~int64_t(3);
+  G = (need + chunk - 1) / chunk;
+  if (G > kMaxChunks || G > max_res) return MI_TOPK_ETOOLONG;
+  const int64_t rows_per_iter = std::min<int64_t>(num_rows, max_res / G);
+  pl->kind = kSplit1024x16;
+  pl->chunk = chunk;
+  pl->G = static_cast<int>(G);
+  pl->rows_per_iter = static_cast<int>(rows_per_iter);
+  pl->grid = rows_per_iter * G;
+  pl->ws_bytes = kWsHeader + static_cast<size_t>(num_rows) * sizeof(RowWs);
+  return MI_TOPK_OK;
+}
+
+int check_shape(int64_t num_rows, int64_t row_stride, int32_t k) {
+  if (num_rows < 0 || num_rows > INT32_MAX) return MI_TOPK_EINVAL;
+  if (row_stride < 1 || row_stride > INT32_MAX - 8) return MI_TOPK_EINVAL;
+  if (k < 1 || k > MI_TOPK_MAX_K) return MI_TOPK_EINVAL;
+  return MI_TOPK_OK;
+}
+
+size_t workspace_size_impl(int64_t num_rows, int64_t row_stride, int32_t k, int path, int chunks) {
+  if (check_shape(num_rows, row_stride, k) != MI_TOPK_OK || num_rows == 0) return 0;
+  DeviceInfo dev;
+  if (device_info(&dev) != hipSuccess) return 0;
+  Plan pl;
+  if (make_plan(num_rows, row_stride, k, path, chunks, 3, dev, &pl) != MI_TOPK_OK) return 0;
+  return pl.ws_bytes;
+}
+
+int launch(const Plan& pl, Params prm, hipStream_t stream) {
+  const KindInfo& ki = kKinds[pl.kind];
+  void* args[] = {&prm};
+  hipError_t e;
+  if (ki.split) {
+    e = hipLaunchCooperativeKernel(ki.fn, dim3(static_cast<unsigned>(pl.grid)), dim3(ki.block), args, 0,
+                                   stream);
+  } else {
+    e = hipLaunchKernel(ki.fn, dim3(static_cast<unsigned>(pl.grid)), dim3(ki.block), args, 0, stream);
+  }
+  return e == hipSuccess ? MI_TOPK_OK : MI_TOPK_ELAUNCH;
+}
+
+int topk_impl(const float* logits, int64_t row_stride, const int32_t* lengths, int64_t num_rows,
+              int32_t k, int32_t* out, void* workspace, size_t workspace_bytes, int path, int chunks,
+              hipStream_t stream) {
+  int st = check_shape(num_rows, row_stride, k);
+  if (st != MI_TOPK_OK) return st;
+  if (path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_SPLIT || chunks < 0) return MI_TOPK_EINVAL;
+  if (num_rows == 0) return MI_TOPK_OK;
+  if (!logits || !lengths || !out) return MI_TOPK_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(logits) & 3u) || (reinterpret_cast<uintptr_t>(lengths) & 3u) ||
+      (reinterpret_cast<uintptr_t>(out) & 3u))
+    return MI_TOPK_EINVAL;
+  DeviceInfo dev;
+  if (device_info(&dev) != hipSuccess) return MI_TOPK_ELAUNCH;
+  const int head_max = ((reinterpret_cast<uintptr_t>(logits) & 15u) == 0 && (row_stride & 3) == 0) ? 0 : 3;
+  Plan pl;
+  st = make_plan(num_rows, row_stride, k, path, chunks, head_max, dev, &pl);
+  if (st != MI_TOPK_OK) return st;
+  if (pl.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < pl.ws_bytes)) return MI_TOPK_EWORKSPACE;
+  Params prm;
+  prm.logits = logits;
+  prm.row_stride = row_stride;
+  prm.lengths = lengths;
+  prm.num_rows = num_rows;
+  prm.out = out;
+  prm.ws = static_cast<uint8_t*>(workspace);
+  prm.k = k;
+  prm.chunk = static_cast<int32_t>(pl.chunk);
+  prm.G = pl.G;
+  prm.rows_per_iter = pl.rows_per_iter;
+  return launch(pl, prm, stream);
+}
+
+}  // namespace
+}  // namespace mitopk
+
+using namespace mitopk;
+
+MI_TOPK_EXPORT size_t topk_workspace_size(int64_t num_rows, int64_t row_stride, int32_t k) {
+  return workspace_size_impl(num_rows, row_stride, k, MI_TOPK_PATH_AUTO, 0);
+}
+
+MI_TOPK_EXPORT size_t topk_workspace_size_path(int64_t num_rows, int64_t row_stride, int32_t k,
+                                               int32_t path, int32_t chunks) {
+  if (path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_SPLIT || chunks < 0) return 0;
+  return workspace_size_impl(num_rows, row_stride, k, path, chunks);
+}
+
+MI_TOPK_EXPORT int topk_indices(const float* logits, int64_t row_stride, const int32_t* lengths,
+                                int64_t num_rows, int32_t k, int32_t* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return topk_impl(logits, row_stride, lengths, num_rows, k, out, workspace, workspace_bytes,
+                   MI_TOPK_PATH_AUTO, 0, stream);
+}
+
+MI_TOPK_EXPORT int topk_indices_path(const float* logits, int64_t row_stride, const int32_t* lengths,
+                                     int64_t num_rows, int32_t k, int32_t* out, void* workspace,
+                                     size_t workspace_bytes, int32_t path, int32_t chunks,
+                                     hipStream_t stream) {
+  return topk_impl(logits, row_stride, lengths, num_rows, k, out, workspace, workspace_bytes, path,
+                   chunks, stream);
+}
+
+MI_TOPK_EXPORT int topk_plan_describe(int64_t num_rows, int64_t row_stride, int32_t k, int32_t path,
+                                      int32_t chunks, int64_t* info) {
+  int st = check_shape(num_rows, row_stride, k);
+  if (st != MI_TOPK_OK) return st;
+  if (!info || path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_SPLIT || chunks < 0) return MI_TOPK_EINVAL;
+  DeviceInfo dev;
+  if (device_info(&dev) != hipSuccess) return MI_TOPK_ELAUNCH;
+  Plan pl;
+  const int head_max = (row_stride & 3) == 0 ? 0 : 3;
+  st = make_plan(num_rows, row_stride, k, path, chunks, head_max, dev, &pl);
+  if (st != MI_TOPK_OK) return st;
+  const KindInfo& ki = kKinds[pl.kind];
+  info[0] = ki.split ? MI_TOPK_PATH_SPLIT : MI_TOPK_PATH_LOCAL;
+  info[1] = ki.block;
+  info[2] = ki.e;
+  info[3] = pl.chunk;
+  info[4] = pl.G;
+  info[5] = pl.grid;
+  info[6] = static_cast<int64_t>(pl.ws_bytes);
+  return MI_TOPK_OK;
+}
+
+MI_TOPK_EXPORT const char* topk_status_string(int status) {
+  switch (status) {
+    case MI_TOPK_OK: return "ok";
+    case MI_TOPK_EINVAL: return "invalid argument";
+    case MI_TOPK_EWORKSPACE: return "workspace too small";
+    case MI_TOPK_ELAUNCH: return "HIP launch or device query failed";
+    case MI_TOPK_ETOOLONG: return "rows too long for the device";
+    default: return "unknown status";
+  }
+}
+
+MI_TOPK_EXPORT int topk_debug_keys(const float* in, uint32_t* out, int64_t n, hipStream_t stream) {
+  if (n < 0 || n > (int64_t(1) << 40)) return MI_TOPK_EINVAL;
+  if (n == 0) return MI_TOPK_OK;
+  if (!in || !out) return MI_TOPK_EINVAL;
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks > INT32_MAX) return MI_TOPK_EINVAL;
+  hipLaunchKernelGGL(debug_keys_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, in, out, n);
+  return hipGetLastError() == hipSuccess ? MI_TOPK_OK : MI_TOPK_ELAUNCH;
+}

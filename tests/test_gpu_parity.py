@@ -1,0 +1,130 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every comparison is element by element on the selected indices (the kernels
+emit ascending order and break ties by lowest index, as the oracle does).
+Outputs are prefilled with a sentinel so unwritten slots show up.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import row_wise_top_topk_amd as mt
+import workloads
+from gpu_util import SENTINEL, assert_parity, device_view, expected, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "strided_example.json")
+
+
+def test_golden_strided_example():
+    d = json.load(open(GOLDEN))
+    flat = torch.tensor([float(v) for r in d["rows"] for v in r], dtype=torch.float32)
+    w = workloads.Workload("golden", flat, d["row_stride"], torch.tensor(d["lengths"], dtype=torch.int32),
+                           len(d["lengths"]), d["k"])
+    for path in ("auto", "local", "split"):
+        got = run_gpu(w, path=path)
+        assert got.tolist() == d["expected"], path
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "long", "prefill", "adversarial"])
+def test_named_workloads_match_oracle(name):
+    w = workloads.make(name)
+    got = run_gpu(w)
+    assert_parity(w, got, label=name)
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3])
+@pytest.mark.parametrize("stride", [4097, 5003, 30001])
+def test_misaligned_base_and_odd_stride(offset, stride):
+    lengths = [1, 5, 511, 512, 513, stride - 3, stride, stride - 1]
+    w = workloads.make_custom(len(lengths), stride, lengths, 512, seed=stride + offset, kind="normal")
+    for path in ("auto", "split"):
+        got = run_gpu(w, path=path, offset=offset)
+        assert_parity(w, got, label=f"{path} off={offset} stride={stride}")
+
+
+@pytest.mark.parametrize("kind", ["normal", "bf16", "levels", "equal", "ramp", "outliers"])
+def test_local_and_split_agree_with_oracle(kind):
+    stride = 20000
+    lengths = [20000, 19999, 17, 2048, 2049, 12345, 4096, 16384]
+    w = workloads.make_custom(len(lengths), stride, lengths, 2048, seed=7, kind=kind)
+    ref = expected(w)
+    for path, chunks in (("local", 0), ("split", 0), ("split", 2), ("split", 3), ("split", 7)):
+        got = run_gpu(w, path=path, chunks=chunks)
+        assert np.array_equal(got, ref), f"{kind} {path} chunks={chunks}"
+
+
+@pytest.mark.parametrize("k", [1, 31, 255, 512, 1023, 1024, 2048, 4096, 9000])
+def test_k_sweep_in_one_process(k):
+    lengths = [30000, 8000, 5000, 1, k, k + 1, max(k - 1, 0), 29999]
+    w = workloads.make_custom(len(lengths), 30016, lengths, k, seed=k, kind="bf16")
+    got = run_gpu(w)
+    assert_parity(w, got, label=f"k={k}")
+    got = run_gpu(w, path="split", chunks=4)
+    assert_parity(w, got, label=f"k={k} split")
+
+
+def test_lengths_are_clamped_and_empty_rows_padded():
+    w = workloads.make_custom(6, 1000, [0, -5, 3000, 1000, 999, 1], 64, seed=3)
+    got = run_gpu(w)
+    w.lengths = w.lengths.clamp(0, 1000)       # what the oracle's definition does
+    assert_parity(w, got, label="clamp")
+    assert np.all(got[0] == -1) and np.all(got[1] == -1)
+
+
+def test_empty_batch_is_a_noop():
+    logits = torch.zeros((0, 128), dtype=torch.float32, device="cuda:0")
+    lengths = torch.zeros((0,), dtype=torch.int32, device="cuda:0")
+    out = mt.topk_indices(logits, lengths, 8)
+    assert out.shape == (0, 8)
+
+
+def test_special_values():
+    stride = 4096
+    rows = []
+    neg0 = np.zeros(stride, dtype=np.float32); neg0[1::2] = -0.0
+    rows.append(neg0)
+    infs = np.full(stride, -np.inf, dtype=np.float32); infs[:5] = [1, 2, 3, 4, 5]
+    rows.append(infs)
+    mixed = np.random.default_rng(5).standard_normal(stride).astype(np.float32)
+    mixed[::7] = 0.0; mixed[3::7] = -0.0; mixed[5::11] = np.inf
+    rows.append(mixed)
+    sub = (np.random.default_rng(6).integers(1, 1 << 23, size=stride, dtype=np.int64)
+           | (np.random.default_rng(7).integers(0, 2, size=stride, dtype=np.int64) << 31))
+    rows.append(sub.astype(np.uint32).view(np.float32))
+    flat = torch.from_numpy(np.concatenate(rows))
+    w = workloads.Workload("special", flat, stride, torch.full((4,), stride, dtype=torch.int32), 4, 300)
+    for path in ("local", "split"):
+        assert_parity(w, run_gpu(w, path=path), label=f"special {path}")
+
+
+def test_random_stress():
+    rng = np.random.default_rng(1234)
+    for trial in range(60):
+        rows = int(rng.integers(1, 40))
+        stride = int(rng.integers(1, 70000))
+        k = int(rng.integers(1, 3000))
+        lengths = rng.integers(-2, stride + 3, size=rows)
+        kind = ["normal", "bf16", "levels", "equal", "outliers"][trial % 5]
+        w = workloads.make_custom(rows, stride, lengths, k, seed=trial, kind=kind)
+        got = run_gpu(w, offset=trial % 4)
+        w.lengths = w.lengths.clamp(0, stride)
+        assert_parity(w, got, label=f"trial {trial} rows={rows} stride={stride} k={k} {kind}")
+
+
+def test_workspace_reuse_across_calls():
+    w = workloads.make_custom(16, 50000, 50000, 1024, seed=9, kind="bf16")
+    logits, lengths = device_view(w)
+    need = mt.workspace_size(16, 50000, 1024, path="split", chunks=5)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    ref = expected(w)
+    for _ in range(5):
+        out = mt.topk_indices(logits, lengths, 1024, workspace=ws, path="split", chunks=5)
+        assert np.array_equal(out.cpu().numpy(), ref)
+    torch.cuda.synchronize()
+    assert mt.workspace_error(ws) == 0
