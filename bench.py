@@ -1,0 +1,229 @@
+"""Benchmark: batched, row-wise, stride-correct top-k index selection on one GPU.
+
+One step = one call of the library's top-k over the whole batch (all rows),
+with the inputs already resident in HBM.  Two copies of the input are used in
+turn so that consecutive steps do not find the previous step's data in the
+256 MB last-level cache.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload prefill]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import multiprocessing as mp
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+METRIC = "rows/s and achieved HBM GB/s (% of peak), batched strided top-k, k=2048"
+DESCRIPTIONS = {
+    "prefill": "causal prefill indexer: 4096 rows, L_i = 28672+i+1, row stride 32768, "
+               "N(0,1) + per-row offset U(-3,3), k=2048",
+    "long": "small-batch long context: 8 rows, L_i = 900000, row stride 900096, "
+            "N(0,1) with 0.5% N(4,1) outliers, k=2048",
+    "decode": "decode batch: 64 rows, L_i ~ U{1..60000}, row stride 60160, bf16-rounded N(0,1), k=1024",
+    "adversarial": "adversarial mix: 256 rows, row stride 131072, k=1024",
+    "tiny": "tiny: 4 rows x 4096, k=512",
+}
+KERNEL_SOURCES = ["row_wise_top_topk_amd/csrc/topk_kernels.hip",
+                  "row_wise_top_topk_amd/csrc/select_device.hpp",
+                  "row_wise_top_topk_amd/csrc/wave64.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------- CPU oracle leg
+_CPU = {}
+
+
+def _oracle_rows(rows):
+    from oracle import oracle_topk_row, row_view
+    w = _CPU["w"]
+    flat = _CPU["flat"]
+    lengths = _CPU["lengths"]
+    for r in rows:
+        oracle_topk_row(row_view(flat, w.row_stride, int(lengths[r]), r), w.k)
+    return len(rows)
+
+
+def cpu_baseline(w, max_rows: int) -> dict:
+    """The CPU oracle, as it stands, over a bounded sample of the same rows."""
+    cores = min(16, len(os.sched_getaffinity(0)))
+    _CPU["w"] = w
+    _CPU["flat"], _CPU["lengths"] = workloads.to_numpy(w)
+    rows = list(range(min(max_rows, w.num_rows)))
+    parts = [rows[i::cores] for i in range(cores)]
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        done = sum(pool.map(_oracle_rows, parts))
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {done} rows of the {w.name} workload, one pass, "
+                      f"numpy stable argsort per row across a {cores}-process pool "
+                      f"({dt:.2f} s wall)"}
+
+
+# ---------------------------------------------------------------- GPU leg
+def gpu_env() -> dict:
+    env = {}
+    try:
+        env["gpu"] = torch.cuda.get_device_name(0)
+    except Exception:
+        pass
+    env["hip"] = getattr(torch.version, "hip", None)
+    try:
+        env["git"] = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT,
+                                    capture_output=True, text=True).stdout.strip() or None
+    except Exception:
+        env["git"] = None
+    return env
+
+
+def time_workload(w, steps: int, warmup: int, copies: int = 2):
+    import row_wise_top_topk_amd as mt
+    dev = torch.device("cuda:0")
+    bufs = []
+    for _ in range(copies):
+        flat = w.flat.to(dev)
+        bufs.append(flat.as_strided((w.num_rows, w.row_stride), (w.row_stride, 1)))
+    lengths = w.lengths.to(dev)
+    out = torch.empty((w.num_rows, w.k), dtype=torch.int32, device=dev)
+    need = mt.workspace_size(w.num_rows, w.row_stride, w.k)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev) if need else None
+    for i in range(warmup):
+        mt.topk_indices(bufs[i % copies], lengths, w.k, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)  # the stream the library launches on
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        mt.topk_indices(bufs[i % copies], lengths, w.k, out=out, workspace=ws)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    total_ms = starts[0].elapsed_time(ends[-1])
+    err = mt.workspace_error(ws) if ws is not None else 0
+    if err:
+        raise RuntimeError("a cross-workgroup barrier wait gave up during the benchmark")
+    return total_ms, per_launch_ms, wall
+
+
+def calibrate_copy() -> None:
+    """A plain copy of known size, to scale the HBM byte counters by."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 5}), flush=True)
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--secondary", default="long",
+                    help="a second workload timed for context ('' to skip)")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="rows of the workload the CPU oracle leg processes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 1 GiB five times (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): rows are independent, "
+              "so the path shards by rows with no exchange; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    w = workloads.make(args.workload)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_rows)   # before the GPU is initialised (fork pool)
+
+    total_ms, per_launch, wall = time_workload(w, args.steps, args.warmup)
+    ms_per_step = total_ms / args.steps
+    alg_bytes = w.algorithmic_bytes()
+    avg_launch_ms = float(np.mean(per_launch))
+    achieved = alg_bytes / (avg_launch_ms * 1e-3) / 1e9
+    rows_per_s = w.num_rows / (ms_per_step * 1e-3)
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        t = json.load(open(TRAFFIC_FILE))
+        if t.get("kernel_hash") == kernel_source_hash() and t.get("workload") == args.workload:
+            traffic = t.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": DESCRIPTIONS[args.workload], "rows": w.num_rows,
+                   "row_stride": w.row_stride, "k": w.k, "valid_elements": w.valid_elements,
+                   "algorithmic_bytes": alg_bytes, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+        "cpu_baseline": cpu,
+        "gbs_per_step": alg_bytes / (ms_per_step * 1e-3) / 1e9,
+        "launch_us": {"mean": avg_launch_ms * 1e3, "p10": float(np.percentile(per_launch, 10)) * 1e3,
+                      "p50": float(np.percentile(per_launch, 50)) * 1e3,
+                      "p90": float(np.percentile(per_launch, 90)) * 1e3},
+        "host_wall_s": wall,
+        "env": gpu_env(),
+    }
+    if args.secondary and args.secondary != args.workload:
+        w2 = workloads.make(args.secondary)
+        t2, pl2, _ = time_workload(w2, args.steps, args.warmup, copies=12)
+        b2 = w2.algorithmic_bytes()
+        m2 = float(np.mean(pl2))
+        result["secondary"] = {"workload": DESCRIPTIONS[args.secondary],
+                               "launch_us_mean": m2 * 1e3,
+                               "launch_us_p50": float(np.percentile(pl2, 50)) * 1e3,
+                               "rows_per_s": w2.num_rows / (t2 / args.steps * 1e-3),
+                               "achieved_gbs": b2 / (m2 * 1e-3) / 1e9,
+                               "frac": b2 / (m2 * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -86,19 +86,23 @@ __device__ __forceinline__ void g_store64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Barrier among the `target / n_instance` workgroups of one row.  Every
-// thread releases its prior global writes at device scope; thread 0 arrives
-// and waits until `target` arrivals are counted.  The wait is bounded: after
-// kSpinLimit polls it sets the sticky error word and gives up, so a wave can
-// never wait forever.
+// Barrier among the workgroups of one row (`target` arrivals in all).
+// Every access to data shared between the row's workgroups (histograms,
+// counts, candidates, this counter) is a device-scope atomic, so it is
+// coherent across the XCDs' L2 caches without cache write-back or
+// invalidation; what the barrier must guarantee is order.  Each wavefront
+// waits until its own atomics and stores have completed, the workgroup
+// synchronises, and thread 0 arrives and polls the counter.  The wait is
+// bounded: after kSpinLimit polls it sets the sticky error word and gives
+// up, so no wave can wait forever.
 __device__ __forceinline__ void row_barrier(uint32_t* bar, uint32_t target, uint32_t* err) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t spins = 0;
-    while (__hip_atomic_load(bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(2);
+    while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(1);
       if (++spins == kSpinLimit) {
         g_store(err, 1u);
         break;
@@ -106,7 +110,7 @@ __device__ __forceinline__ void row_barrier(uint32_t* bar, uint32_t target, uint
     }
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  asm volatile("" ::: "memory");
 }
 
 // A chunk of a row held in registers: NS = E/4 slots of 16 bytes per thread.
@@ -505,23 +509,23 @@ __global__ void __launch_bounds__(BLOCK) topk_split_kernel(Params p) {
     emit_ordered<BLOCK, E>(key, ch, pf, ib, out_row, off, static_cast<uint32_t>(p.k), lds_scan);
 
     // Leave the row; the last workgroup out returns its workspace to zero.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // Every read of the row's shared data happened before this arrival.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
-      const uint32_t old = __hip_atomic_fetch_add(&ws->bar, 1u, __ATOMIC_ACQ_REL,
+      const uint32_t old = __hip_atomic_fetch_add(&ws->bar, 1u, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
       res[3] = old == (nbar + 1) * nwg - 1u ? 1u : 0u;
     }
     __syncthreads();
     if (res[3]) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       for (int r = 0; r < rounds_used; ++r) {
         const int nbins = r == 0 ? kFirstBins : kNextBins;
         uint32_t* gh = ws->hist + hist_offset(r);
         for (int i = tid; i < nbins; i += BLOCK) g_store(&gh[i], 0u);
       }
       if (tid == 0) g_store(&ws->cand_count, 0u);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (tid == 0) g_store(&ws->bar, 0u);
     }
