@@ -121,12 +121,17 @@ __device__ __forceinline__ void with_pred(const Prefix& p, int ib, uint32_t rmas
 }
 
 // Histogram one digit (d bits, below prefix p) of the entries in p's bucket,
-// for entries produced by `for_each(f)` calling f(key, j).  p.bits > 0.
+// for entries produced by `for_each(f)` calling f(key, j).
 template <class ForEach>
 __device__ __forceinline__ void count_digit(ForEach for_each, const Prefix& p, int d, int ib,
                                             uint32_t rmask, uint32_t* hist) {
   const uint32_t dmask = (1u << d) - 1u;
-  if (p.bits < 32) {
+  if (p.bits == 0) {
+    const int sh = 32 - d;
+    for_each([&](uint32_t key, int32_t) {
+      if (key != 0u) atomicAdd(&hist[key >> sh], 1u);
+    });
+  } else if (p.bits < 32) {
     const int sh = 32 - p.bits;
     const int dsh = sh - d;
     const uint32_t kp = p.kp;
@@ -189,6 +194,94 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, int nb, uint32
   __syncthreads();
 }
 
+// The same search done by the calling wavefront alone (the other wavefronts
+// of the workgroup need not take part), in two levels: lane l first sums a
+// group of NB/64 adjacent bins (group l counted from the top, read with
+// 16-byte LDS loads), a wavefront prefix sum finds the group holding the
+// need-th entry, and then lane i reads bin i of that group and a second
+// prefix sum finds the bin.  need_of(total) gives `need` from the
+// histogram's total (so a caller can derive it from the count).  The result
+// goes to res[0..2]; the caller synchronises before reading it.  Returns the
+// histogram total.
+template <int NB, class NeedOf>
+__device__ __forceinline__ uint32_t find_bucket_wave_nb(const uint32_t* hist, NeedOf need_of,
+                                                        uint32_t* res) {
+  static_assert(NB >= 4 && (NB & (NB - 1)) == 0, "power-of-two bin count");
+  constexpr int GS = NB >= kWave ? NB / kWave : 1;      // bins per group
+  constexpr int GROUPS = NB / GS;
+  const int lane = static_cast<int>(__lane_id());
+  uint32_t s = 0;
+  if (lane < GROUPS) {
+    const int lo = NB - (lane + 1) * GS;                 // group [lo, lo + GS)
+    if constexpr (GS >= 4) {
+      // batches of at most four 16-byte loads in flight (few registers)
+      constexpr int NV = GS / 4;
+      constexpr int BATCH = NV < 4 ? NV : 4;
+      const uint4* h4 = reinterpret_cast<const uint4*>(hist + lo);
+#pragma unroll 1
+      for (int b = 0; b < NV; b += BATCH) {
+        uint4 v[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) v[i] = h4[b + i];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) s += v[i].x + v[i].y + v[i].z + v[i].w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < GS; ++i) s += hist[lo + i];
+    }
+  }
+  const uint32_t incl = wave_inclusive_sum(s);
+  const uint32_t total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+  const uint32_t need = need_of(total);
+  if (need == 0u || need > total) return total;
+  const uint64_t crossed = __ballot(incl >= need);
+  const int g = __ffsll(static_cast<unsigned long long>(crossed)) - 1;   // first group reaching need
+  const uint32_t above_g = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl - s), g));
+  // second level: lane i takes bin i of group g, counted from the group's top
+  const int bin = NB - g * GS - 1 - lane;
+  const uint32_t h = lane < GS ? hist[bin] : 0u;
+  const uint32_t incl2 = above_g + wave_inclusive_sum(h);
+  const uint64_t crossed2 = __ballot(lane < GS && incl2 >= need);
+  const int c = __ffsll(static_cast<unsigned long long>(crossed2)) - 1;
+  if (lane == c) {
+    res[0] = static_cast<uint32_t>(bin);
+    res[1] = incl2 - h;
+    res[2] = h;
+  }
+  return total;
+}
+
+// find_bucket_wave_nb for a bin count known only at run time (a power of two
+// from 2 to 4096).
+__device__ __forceinline__ void find_bucket_wave(const uint32_t* hist, int nb, uint32_t need,
+                                                 uint32_t* res) {
+  auto fixed = [need](uint32_t) { return need; };
+  switch (nb) {
+    case 4096: find_bucket_wave_nb<4096>(hist, fixed, res); break;
+    case 1024: find_bucket_wave_nb<1024>(hist, fixed, res); break;
+    case 512: find_bucket_wave_nb<512>(hist, fixed, res); break;
+    case 256: find_bucket_wave_nb<256>(hist, fixed, res); break;
+    case 128: find_bucket_wave_nb<128>(hist, fixed, res); break;
+    case 64: find_bucket_wave_nb<64>(hist, fixed, res); break;
+    case 32: find_bucket_wave_nb<32>(hist, fixed, res); break;
+    case 16: find_bucket_wave_nb<16>(hist, fixed, res); break;
+    case 8: find_bucket_wave_nb<8>(hist, fixed, res); break;
+    case 4: find_bucket_wave_nb<4>(hist, fixed, res); break;
+    default: {  // nb == 2
+      const int lane = static_cast<int>(__lane_id());
+      if (lane == 0) {
+        const uint32_t h1 = hist[1], h0 = hist[0];
+        if (h1 >= need) {
+          res[0] = 1u; res[1] = 0u; res[2] = h1;
+        } else {
+          res[0] = 0u; res[1] = h1; res[2] = h0;
+        }
+      }
+    }
+  }
+}
+
 // Radix rounds inside one workgroup.  `src.count(p, d, ib, rmask, hist)`
 // histograms digit d below prefix p (p.bits == 0: all entries).  Starting
 // from prefix p with `need` entries still to choose among p's bucket, the
@@ -196,8 +289,8 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, int nb, uint32
 // entry contains exactly `need` entries.  Returns the final prefix: the
 // selected entries are those whose composite prefix is >= it.
 template <int BLOCK, class Src>
-__device__ Prefix rounds_local(const Src& src, Prefix p, uint32_t need, int ib, uint32_t* hist,
-                               uint32_t* lds_scan, uint32_t* res) {
+__device__ __forceinline__ Prefix rounds_local(const Src& src, Prefix p, uint32_t need, int ib,
+                                               uint32_t* hist, uint32_t* res) {
   const uint32_t rmask = (1u << ib) - 1u;
   for (int round = 0; round < kMaxRounds + 1; ++round) {
     const int d = digit_bits(p.bits, ib);
@@ -206,7 +299,8 @@ __device__ Prefix rounds_local(const Src& src, Prefix p, uint32_t need, int ib, 
     __syncthreads();
     src.count(p, d, ib, rmask, hist);
     __syncthreads();
-    find_bucket<BLOCK>(hist, nb, need, lds_scan, res);
+    if (threadIdx.x < kWave) find_bucket_wave(hist, nb, need, res);
+    __syncthreads();
     const uint32_t b = res[0], gt = res[1], cnt = res[2];
     need -= gt;
     p = extend(p, d, b);

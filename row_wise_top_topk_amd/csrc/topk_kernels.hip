@@ -113,15 +113,22 @@ __device__ __forceinline__ void row_barrier(uint32_t* bar, uint32_t target, uint
   asm volatile("" ::: "memory");
 }
 
-// A chunk of a row held in registers: NS = E/4 slots of 16 bytes per thread.
-// Slot s of thread t covers chunk elements 4q..4q+3 with q = s*BLOCK + t, so
-// each load instruction of a wavefront reads 1 KiB of consecutive memory.
-// Elements are addressed from the 16-byte-aligned address at or below the
-// row start; element e of the chunk is column jbase + e of the row.
+// ---------------------------------------------------------------------------
+// Register layout of a chunk.
+//
+// Thread t = 64*w + l (wavefront w, lane l) of a workgroup holds E elements.
+// Its element at position u (0 <= u < E) is chunk element
+//     e = w*64*E + u*64 + l,
+// so every wavefront owns one contiguous stretch of 64*E elements, each of
+// its load instructions reads 256 consecutive bytes, and in (wavefront,
+// position, lane) order the elements are in column order.  That order is
+// what lets the kernels place selected elements with a wavefront ballot and
+// still write them in ascending column order.  Element e of the chunk is
+// column jbase + e of the row.
+// ---------------------------------------------------------------------------
 struct Chunk {
-  const float* base;  // 16-byte aligned
+  const float* base;  // element 0 of the chunk (the row start minus head, for chunk 0)
   int llo, lhi;       // valid elements [llo, lhi) of the chunk (llo <= 3)
-  int hi_slot;        // slots [0, hi_slot) hold at least one valid element
   int32_t jbase;
 };
 
@@ -131,59 +138,81 @@ __device__ __forceinline__ Chunk make_chunk(const float* row_ptr, int head, int6
   ch.base = row_ptr - head + cbase;
   ch.llo = llo;
   ch.lhi = lhi;
-  ch.hi_slot = (lhi + 3) >> 2;
   ch.jbase = static_cast<int32_t>(cbase - head);
   return ch;
 }
 
-// Loads the chunk and converts it to keys.  All loads are issued before any
-// is consumed (no branch between them), through a buffer resource whose
-// bound is the end of the last slot holding a valid element: lanes past it
-// read zeros without touching memory.  Entries outside [llo, lhi) are then set to key 0;
-// that test is uniform for every slot row except the one or two that hold
-// the row's start or end.
-template <int BLOCK, int E>
-__device__ __forceinline__ void load_keys(uint32_t (&key)[E], const Chunk& ch) {
-  constexpr int NS = E / 4;
-  const int tid = threadIdx.x;
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(ch.base), 0, ch.hi_slot * 16, 0x00020000);
-  using u32x4 = __attribute__((ext_vector_type(4))) uint32_t;
-  u32x4 raw[NS];
-  // The whole byte offset goes in the vector offset: that is the part the
-  // hardware range-checks against the resource's size (the scalar offset is
-  // not checked), so slots past the bound are never read.
+__device__ __forceinline__ uint32_t wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
+
+// This thread's element at position 0 (w*64*E + l), derived afresh on every
+// call through an empty asm statement so that the compiler does not keep one
+// position register per element alive across the callers' loops.
+template <int E>
+__device__ __forceinline__ int thread_elem0() {
+  int e = static_cast<int>(wave_id()) * (kWave * E) + static_cast<int>(__lane_id());
+  asm volatile("" : "+v"(e));
+  return e;
+}
+
+// Marks positions outside [llo, lhi): fn(u, e) is called for every position
+// u of a wavefront row that holds the chunk's start or end (the test is
+// uniform across the wavefront for every other row), and `beyond(u)` for
+// rows entirely past the end.
+template <int E, class Partial, class Beyond>
+__device__ __forceinline__ void for_boundary_positions(const Chunk& ch, Partial partial,
+                                                       Beyond beyond) {
+  const int e_wave = static_cast<int>(wave_id()) * (kWave * E);
+  const int e0 = thread_elem0<E>();
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-    raw[s] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (s * BLOCK + tid) * 16, 0, 0);
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) key[4 * s + c] = order_key_bits(raw[s][c]);
-  }
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int e_first = s * BLOCK * 4;
+  for (int u = 0; u < E; ++u) {
+    const int e_first = e_wave + u * kWave;
     if (e_first >= ch.lhi) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) key[4 * s + c] = 0u;
-    } else if (e_first + BLOCK * 4 > ch.lhi || e_first < ch.llo) {
-      const int e0 = 4 * (s * BLOCK + tid);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bool ok = e0 + c >= ch.llo && e0 + c < ch.lhi;
-        key[4 * s + c] = ok ? key[4 * s + c] : 0u;
-      }
+      beyond(u);
+    } else if (e_first + kWave > ch.lhi || e_first < ch.llo) {
+      partial(u, e0 + u * kWave);
     }
   }
 }
 
-// The register-held chunk as a source of (key, column) entries.  Slots with
-// no valid element hold key 0, which no prefix test accepts, so the generic
-// passes visit every slot without a bounds test.  The column base goes
-// through an empty asm statement so that the compiler derives the columns
-// afresh at each use instead of keeping one register per element alive
-// across the radix rounds.
+// Raw float bits of entries outside the row: a negative NaN pattern whose
+// key (1) is below every filter bound used here.
+constexpr uint32_t kOutsideBits = 0xFFFFFFFFu;
+
+// Loads the chunk's raw float bits.  All loads are issued before any is
+// consumed (no branch between them), through a buffer resource whose bound
+// is the chunk's last valid element: lanes past it read zeros without
+// touching memory (the byte offset is in the range-checked vector offset).
+// Positions outside [llo, lhi) then get kOutsideBits.
+template <int BLOCK, int E>
+__device__ __forceinline__ void load_raw(uint32_t (&raw)[E], const Chunk& ch) {
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(ch.base), 0, ch.lhi * 4, 0x00020000);
+  const int e0 = static_cast<int>(wave_id()) * (kWave * E) + static_cast<int>(__lane_id());
+#pragma unroll
+  for (int u = 0; u < E; ++u)
+    raw[u] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (e0 + u * kWave) * 4, 0, 0);
+  for_boundary_positions<E>(
+      ch,
+      [&](int u, int e) { raw[u] = (e >= ch.llo && e < ch.lhi) ? raw[u] : kOutsideBits; },
+      [&](int u) { raw[u] = kOutsideBits; });
+}
+
+// Replaces raw bits by their order-preserving keys, in place; entries
+// outside the row get key 0 (decided by position, so a row value equal to
+// kOutsideBits stays valid).
+template <int BLOCK, int E>
+__device__ __forceinline__ void keys_in_place(uint32_t (&v)[E], const Chunk& ch) {
+#pragma unroll
+  for (int u = 0; u < E; ++u) v[u] = order_key_bits(v[u]);
+  for_boundary_positions<E>(
+      ch, [&](int u, int e) { v[u] = (e >= ch.llo && e < ch.lhi) ? v[u] : 0u; },
+      [&](int u) { v[u] = 0u; });
+}
+
+// The register-held chunk (keys) as a source of (key, column) entries.
+// Entries outside the row hold key 0, which no prefix test accepts.
 template <int BLOCK, int E>
 struct RegSource {
   const uint32_t (&key)[E];
@@ -191,42 +220,31 @@ struct RegSource {
 
   template <class F>
   __device__ __forceinline__ void operator()(F f) const {
-    constexpr int NS = E / 4;
-    int32_t jt = ch.jbase + 4 * static_cast<int32_t>(threadIdx.x);
-    asm volatile("" : "+v"(jt));
+    const int32_t j0 = ch.jbase + thread_elem0<E>();
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) f(key[4 * s + c], jt + 4 * s * BLOCK + c);
-    }
+    for (int u = 0; u < E; ++u) f(key[u], j0 + u * kWave);
   }
 
-  // Histogram of digit d below prefix p.  For the first digit every loaded
-  // slot is counted without a per-entry test; the few entries outside the
-  // row in the first and last slot (key 0, bin 0) are subtracted again.
+  // Histogram of digit d below prefix p; the first digit is counted without
+  // a per-entry test on rows of the wavefront that are entirely inside the
+  // chunk's valid range.
   __device__ __forceinline__ void count(const Prefix& p, int d, int ib, uint32_t rmask,
                                         uint32_t* hist) const {
     if (p.bits != 0) {
       count_digit(*this, p, d, ib, rmask, hist);
       return;
     }
-    constexpr int NS = E / 4;
     const int sh = 32 - d;
-    const int tid = threadIdx.x;
+    const int e_wave = static_cast<int>(wave_id()) * (kWave * E);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int e_first = s * BLOCK * 4;
-      if (e_first + BLOCK * 4 <= ch.lhi) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) atomicAdd(&hist[key[4 * s + c] >> sh], 1u);
+    for (int u = 0; u < E; ++u) {
+      const int e_first = e_wave + u * kWave;
+      if (e_first >= ch.llo && e_first + kWave <= ch.lhi) {
+        atomicAdd(&hist[key[u] >> sh], 1u);
       } else if (e_first < ch.lhi) {
-        if (s * BLOCK + tid < ch.hi_slot) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) atomicAdd(&hist[key[4 * s + c] >> sh], 1u);
-        }
+        if (key[u] != 0u) atomicAdd(&hist[key[u] >> sh], 1u);
       }
     }
-    if (tid == 0) atomicSub(&hist[0], static_cast<uint32_t>(4 * ch.hi_slot - (ch.lhi - ch.llo)));
   }
 };
 
@@ -248,59 +266,62 @@ struct ListSource {
   }
 };
 
-// Writes the chunk's selected elements (composite prefix >= p) to
-// out_row[base ...] in ascending column order.  The per-slot counts of a
-// thread (at most 4 each) are packed two to a word in 16-bit fields, so one
-// workgroup prefix sum gives every slot of every thread its output position
-// (slot-major, then thread, then lane is column order).
+// Per-thread selected count over the register-held chunk.
 template <int BLOCK, int E, class Pred>
-__device__ __forceinline__ void emit_ordered_pred(const uint32_t (&key)[E], const Chunk& ch,
-                                                  const Pred& pred, int32_t* out_row, uint32_t base,
-                                                  uint32_t limit, uint32_t* lds_scan) {
-  constexpr int NS = E / 4;
-  constexpr int NP = (NS + 1) / 2;
-  const int tid = threadIdx.x;
-  int32_t jt = ch.jbase + 4 * tid;
-  asm volatile("" : "+v"(jt));
-  uint32_t packed[NP];
+__device__ __forceinline__ uint32_t count_ge(const uint32_t (&key)[E], const Chunk& ch,
+                                             const Pred& pred) {
+  uint32_t n = 0;
+  RegSource<BLOCK, E>{key, ch}([&](uint32_t kk, int32_t j) { n += pred.ge(kk, j) ? 1u : 0u; });
+  return n;
+}
+
+// Offset of this wavefront's output: sum of the earlier wavefronts' counts
+// (wtot: one LDS word per wavefront; contains a workgroup barrier).
+template <int BLOCK>
+__device__ __forceinline__ uint32_t wave_offset(uint32_t wave_count, uint32_t* wtot) {
+  constexpr int NW = BLOCK / kWave;
+  const uint32_t w = wave_id();
+  if (__lane_id() == 0) wtot[w] = wave_count;
+  __syncthreads();
+  uint32_t off = 0;
 #pragma unroll
-  for (int i = 0; i < NP; ++i) packed[i] = 0;
+  for (int i = 0; i < NW; ++i) off += (static_cast<uint32_t>(i) < w) ? wtot[i] : 0u;
+  return off;
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+// Writes the chunk's selected elements (pred.ge) to out_row[base ...] in
+// ascending column order: a first pass counts each wavefront's selections,
+// then each position's selected lanes are placed with a ballot.
+template <int BLOCK, int E, class Pred>
+__device__ __forceinline__ void emit_regs(const uint32_t (&key)[E], const Chunk& ch,
+                                          const Pred& pred, int32_t* out_row, uint32_t base,
+                                          uint32_t limit, uint32_t* wtot) {
+  const uint32_t n = count_ge<BLOCK, E>(key, ch, pred);
+  uint32_t pos_wave = base + wave_offset<BLOCK>(wave_sum(n), wtot);
+  const int32_t j0 = ch.jbase + thread_elem0<E>();
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (pred.ge(key[4 * s + c], jt + 4 * s * BLOCK + c)) packed[s >> 1] += 1u << ((s & 1) * 16);
-    }
-  }
-  uint32_t incl[NP], tot[NP];
-#pragma unroll
-  for (int i = 0; i < NP; ++i) incl[i] = packed[i];
-  block_inclusive_sum<BLOCK, NP>(incl, tot, lds_scan);
-  asm volatile("" : "+v"(jt));
-  uint32_t run = base;
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int sh = (s & 1) * 16;
-    uint32_t pos = run + (((incl[s >> 1] - packed[s >> 1]) >> sh) & 0xFFFFu);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int32_t j = jt + 4 * s * BLOCK + c;
-      if (pred.ge(key[4 * s + c], j)) {
-        if (pos < limit) out_row[pos] = j;
-        ++pos;
-      }
-    }
-    run += (tot[s >> 1] >> sh) & 0xFFFFu;
+  for (int u = 0; u < E; ++u) {
+    const int32_t j = j0 + u * kWave;
+    const bool sel = pred.ge(key[u], j);
+    const uint64_t m = __ballot(sel);
+    const uint32_t pos = pos_wave + lanes_below(m);
+    if (sel && pos < limit) out_row[pos] = j;
+    pos_wave += static_cast<uint32_t>(__popcll(m));
   }
 }
 
 template <int BLOCK, int E>
 __device__ __forceinline__ void emit_ordered(const uint32_t (&key)[E], const Chunk& ch,
                                              const Prefix& p, int ib, int32_t* out_row,
-                                             uint32_t base, uint32_t limit, uint32_t* lds_scan) {
+                                             uint32_t base, uint32_t limit, uint32_t* wtot) {
   const uint32_t rmask = (1u << ib) - 1u;
   with_pred(p, ib, rmask, [&](const auto& pred) {
-    emit_ordered_pred<BLOCK, E>(key, ch, pred, out_row, base, limit, lds_scan);
+    emit_regs<BLOCK, E>(key, ch, pred, out_row, base, limit, wtot);
   });
 }
 
@@ -318,26 +339,201 @@ __device__ __forceinline__ int row_length(const Params& p, int64_t row) {
   return static_cast<int>(L < 0 ? 0 : (L > p.row_stride ? p.row_stride : L));
 }
 
-// One row (or one chunk that holds a whole row) entirely inside the workgroup.
+// ---------------------------------------------------------------------------
+// Whole row in one workgroup: sampled filter, then exact selection on the
+// filtered list.
+//
+// Only entries at or above the m-th largest can be selected.  A sample of
+// the row (4 entries per thread, spread over the row) gives a key bound LB
+// such that, with a wide margin, at least k entries of the row are >= LB.
+// One pass over the raw bits then copies the entries >= LB (typically
+// 10-15 % of a long row) into an LDS list in column order, and the key
+// transform, every radix round and the ordered emission run on that list
+// instead of on the whole row.  If fewer than k entries are >= LB, or more
+// than the list holds, the row is selected from the registers instead
+// (always exact; only slower).
+// ---------------------------------------------------------------------------
+constexpr int kListPerThread = 12;
+
+// LDS list: wavefront w's region is [w*kRegionStride, ... + count_w); each
+// region is followed by one spare slot per lane, where lanes with nothing to
+// store write instead (so the copy needs no branch).
+constexpr int kRegion = kWave * kListPerThread;
+constexpr int kRegionStride = kRegion + kWave;
+
+template <int BLOCK>
+struct __attribute__((aligned(16))) RowLds {
+  uint32_t hist[kFirstBins];
+  uint32_t lraw[(BLOCK / kWave) * kRegionStride];
+  uint16_t lcol[(BLOCK / kWave) * kRegionStride];
+  uint32_t wtot[BLOCK / kWave];
+  uint32_t res[4];
+};
+
+// The filtered list, kListPerThread entries per thread in registers: thread
+// t holds list entries [t*per, t*per + per) (column order); unused entries
+// have key 0.
+struct RegList {
+  uint32_t key[kListPerThread];
+  int32_t col[kListPerThread];
+  template <class F>
+  __device__ __forceinline__ void operator()(F f) const {
+#pragma unroll
+    for (int u = 0; u < kListPerThread; ++u) f(key[u], col[u]);
+  }
+  __device__ __forceinline__ void count(const Prefix& p, int d, int ib, uint32_t rmask,
+                                        uint32_t* hist) const {
+    count_digit(*this, p, d, ib, rmask, hist);
+  }
+};
+
+// Sample-based bound.  Each thread contributes 4 entries (one from each
+// quarter of its positions); the bound is the lower edge of the first-digit
+// bin where the sample's count from the top reaches 5/4 of its share of k
+// plus 8.  Returns a key >= 2.
 template <int BLOCK, int E>
-__device__ __forceinline__ void select_whole_row(const uint32_t (&key)[E], const Chunk& ch, int L,
-                                                 int k, int32_t* out_row, uint32_t* hist,
-                                                 uint32_t* lds_scan, uint32_t* res) {
+__device__ __forceinline__ uint32_t sample_bound(const uint32_t (&raw)[E], int L, int k,
+                                                 RowLds<BLOCK>& lds) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kFirstBins; i += BLOCK) lds.hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int qd = 0; qd < 4; ++qd) {
+    const uint32_t key = order_key_bits(raw[qd * E / 4]);
+    if (key > 1u) atomicAdd(&lds.hist[key >> (32 - kFirstBits)], 1u);
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    if (tid == 0) lds.res[0] = 0u;  // no bound unless the sample is large enough
+    // from the sample size ns, need_s = ceil(5 k ns / 4 L) + 8
+    find_bucket_wave_nb<kFirstBins>(
+        lds.hist,
+        [&](uint32_t ns) {
+          return static_cast<uint32_t>((5ull * static_cast<uint64_t>(k) * ns + 4ull * L - 1) /
+                                       (4ull * L)) + 8u;
+        },
+        lds.res);
+  }
+  __syncthreads();
+  const uint32_t lb = lds.res[0] << (32 - kFirstBits);
+  return lb < 2u ? 2u : lb;
+}
+
+// Copies the entries whose key is >= lb (tested on the raw bits) into
+// wavefront w's region of the LDS list, in column order, and returns the
+// wavefront's count (entries past the region's size are counted, not
+// stored).  For lb <= 0x80000000 a value passes iff its bits, unsigned, are
+// <= 2^32 - lb; above that, iff its bits, signed, are >= the bound's bits.
+template <int BLOCK, int E, bool kPositiveBound>
+__device__ __forceinline__ uint32_t filter_wave(const uint32_t (&raw)[E], const Chunk& ch,
+                                                uint32_t lb, RowLds<BLOCK>& lds) {
+  const uint32_t w = wave_id();
+  uint32_t* rraw = lds.lraw + w * kRegionStride;
+  uint16_t* rcol = lds.lcol + w * kRegionStride;
+  const uint32_t spare = kRegion + __lane_id();
+  const uint32_t ulim = 0u - lb;
+  const int32_t slim = static_cast<int32_t>(lb & 0x7FFFFFFFu);
+  const int32_t j0 = ch.jbase + thread_elem0<E>();
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int u = 0; u < E; ++u) {
+    const uint32_t x = raw[u];
+    const bool hit = kPositiveBound ? static_cast<int32_t>(x) >= slim : x <= ulim;
+    const uint64_t m = __ballot(hit);
+    const uint32_t pos = cnt + lanes_below(m);
+    const uint32_t a = (hit && pos < static_cast<uint32_t>(kRegion)) ? pos : spare;
+    rraw[a] = x;
+    rcol[a] = static_cast<uint16_t>(j0 + u * kWave);
+    cnt += static_cast<uint32_t>(__popcll(m));
+  }
+  return cnt;
+}
+
+// Exact selection of a whole row held by this workgroup (L > k), with the
+// selected columns written to out_row in ascending order.
+template <int BLOCK, int E>
+__device__ __forceinline__ void select_row(uint32_t (&raw)[E], const Chunk& ch, int L, int k,
+                                           int32_t* out_row, RowLds<BLOCK>& lds) {
+  constexpr int NW = BLOCK / kWave;
   const int ib = index_bits(L);
-  const uint32_t m = static_cast<uint32_t>(k);  // L > k here
-  const Prefix pf = rounds_local<BLOCK>(RegSource<BLOCK, E>{key, ch}, Prefix{0, 0u, 0u}, m, ib,
-                                        hist, lds_scan, res);
-  emit_ordered<BLOCK, E>(key, ch, pf, ib, out_row, 0u, m, lds_scan);
+  const uint32_t rmask = (1u << ib) - 1u;
+  const uint32_t kk = static_cast<uint32_t>(k);
+  bool done = false;
+  if (L >= 4 * k) {
+    const uint32_t lb = sample_bound<BLOCK, E>(raw, L, k, lds);
+    const uint32_t cw = lb > 0x80000000u ? filter_wave<BLOCK, E, true>(raw, ch, lb, lds)
+                                         : filter_wave<BLOCK, E, false>(raw, ch, lb, lds);
+    if (__lane_id() == 0) lds.wtot[wave_id()] = cw;
+    __syncthreads();
+    uint32_t total = 0, over = 0;
+    uint32_t pre[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const uint32_t c = lds.wtot[i];
+      pre[i] = total;
+      total += c;
+      over |= c > static_cast<uint32_t>(kRegion) ? 1u : 0u;
+    }
+    if (!over && total >= kk) {
+      // the list in registers: entry i of the concatenated regions is at
+      // region w(i), offset i - pre[w(i)]
+      const uint32_t per = (total + BLOCK - 1) / BLOCK;
+      const uint32_t first = threadIdx.x * per;
+      RegList lst;
+#pragma unroll
+      for (int u = 0; u < kListPerThread; ++u) {
+        const uint32_t i = first + u;
+        uint32_t rw = 0, rp = 0;
+#pragma unroll
+        for (int r = 1; r < NW; ++r) {
+          if (i >= pre[r]) {
+            rw = r;
+            rp = pre[r];
+          }
+        }
+        const bool ok = static_cast<uint32_t>(u) < per && i < total;
+        const uint32_t a = rw * kRegionStride + (i - rp);
+        lst.key[u] = ok ? order_key_bits(lds.lraw[a]) : 0u;
+        lst.col[u] = ok ? static_cast<int32_t>(lds.lcol[a]) : 0;
+      }
+      const Prefix pf = rounds_local<BLOCK>(lst, Prefix{0, 0u, 0u}, kk, ib, lds.hist, lds.res);
+      with_pred(pf, ib, rmask, [&](const auto& pred) {
+        uint32_t n = 0;
+#pragma unroll
+        for (int u = 0; u < kListPerThread; ++u) n += pred.ge(lst.key[u], lst.col[u]) ? 1u : 0u;
+        const uint32_t incl = wave_inclusive_sum(n);
+        const uint32_t wtotal =
+            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+        uint32_t pos = wave_offset<BLOCK>(wtotal, lds.wtot) + incl - n;
+#pragma unroll
+        for (int u = 0; u < kListPerThread; ++u) {
+          if (pred.ge(lst.key[u], lst.col[u])) {
+            if (pos < kk) out_row[pos] = lst.col[u];
+            ++pos;
+          }
+        }
+      });
+      done = true;
+    }
+    __syncthreads();  // LDS is reused below
+  }
+  if (!done) {
+    keys_in_place<BLOCK, E>(raw, ch);
+    const Prefix pf =
+        rounds_local<BLOCK>(RegSource<BLOCK, E>{raw, ch}, Prefix{0, 0u, 0u}, kk, ib, lds.hist, lds.res);
+    emit_ordered<BLOCK, E>(raw, ch, pf, ib, out_row, 0u, kk, lds.wtot);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Local path: one workgroup per row, whole row in registers.
 // ---------------------------------------------------------------------------
+// Two workgroups per CU (4 wavefronts per SIMD) let one workgroup's loads
+// overlap the other's selection.
 template <int BLOCK, int E>
-__global__ void __launch_bounds__(BLOCK) topk_local_kernel(Params p) {
-  __shared__ uint32_t hist[kFirstBins];
-  __shared__ uint32_t lds_scan[scan_lds_words<BLOCK, 8>()];
-  __shared__ uint32_t res[4];
+__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+topk_row_kernel(Params p) {
+  __shared__ RowLds<BLOCK> lds;
   const int64_t row = blockIdx.x;
   const int L = row_length(p, row);
   int32_t* out_row = p.out + row * static_cast<int64_t>(p.k);
@@ -348,9 +544,9 @@ __global__ void __launch_bounds__(BLOCK) topk_local_kernel(Params p) {
   const float* row_ptr = p.logits + row * p.row_stride;
   const int head = static_cast<int>((reinterpret_cast<uintptr_t>(row_ptr) >> 2) & 3u);
   const Chunk ch = make_chunk(row_ptr, head, 0, head, head + L);
-  uint32_t key[E];
-  load_keys<BLOCK, E>(key, ch);
-  select_whole_row<BLOCK, E>(key, ch, L, p.k, out_row, hist, lds_scan, res);
+  uint32_t raw[E];
+  load_raw<BLOCK, E>(raw, ch);
+  select_row<BLOCK, E>(raw, ch, L, p.k, out_row, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -359,18 +555,36 @@ __global__ void __launch_bounds__(BLOCK) topk_local_kernel(Params p) {
 
 // Sum over the workgroup of one value per thread (every thread gets it).
 template <int BLOCK>
-__device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* lds_scan) {
-  uint32_t v[1] = {x}, tot[1];
-  block_inclusive_sum<BLOCK, 1>(v, tot, lds_scan);
-  return tot[0];
+__device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* wtot) {
+  const uint32_t ws = wave_sum(x);
+  const uint32_t w = wave_id();
+  if (__lane_id() == 0) wtot[w] = ws;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int i = 0; i < BLOCK / kWave; ++i) t += wtot[i];
+  __syncthreads();
+  return t;
+}
+
+template <int BLOCK, int E>
+__device__ __forceinline__ void select_chunk_whole_row(const uint32_t (&key)[E], const Chunk& ch,
+                                                       int L, int k, int32_t* out_row,
+                                                       uint32_t* hist, uint32_t* wtot,
+                                                       uint32_t* res) {
+  const int ib = index_bits(L);
+  const uint32_t kk = static_cast<uint32_t>(k);
+  const Prefix pf =
+      rounds_local<BLOCK>(RegSource<BLOCK, E>{key, ch}, Prefix{0, 0u, 0u}, kk, ib, hist, res);
+  emit_ordered<BLOCK, E>(key, ch, pf, ib, out_row, 0u, kk, wtot);
 }
 
 template <int BLOCK, int E>
 __global__ void __launch_bounds__(BLOCK) topk_split_kernel(Params p) {
-  __shared__ uint32_t hist[kFirstBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kFirstBins];
   __shared__ uint64_t cand[kCandCap];
   __shared__ uint32_t csel[kMaxChunks];
-  __shared__ uint32_t lds_scan[scan_lds_words<BLOCK, 8>()];
+  __shared__ uint32_t wtot[BLOCK / kWave];
   __shared__ uint32_t res[4];
   const int tid = threadIdx.x;
   const int G = p.G;
@@ -397,9 +611,10 @@ __global__ void __launch_bounds__(BLOCK) topk_split_kernel(Params p) {
     const Chunk ch = make_chunk(row_ptr, head, cbase, g == 0 ? head : 0,
                                 static_cast<int>(span - cbase < p.chunk ? span - cbase : p.chunk));
     uint32_t key[E];
-    load_keys<BLOCK, E>(key, ch);
+    load_raw<BLOCK, E>(key, ch);
+    keys_in_place<BLOCK, E>(key, ch);
     if (Gr == 1) {
-      select_whole_row<BLOCK, E>(key, ch, L, p.k, out_row, hist, lds_scan, res);
+      select_chunk_whole_row<BLOCK, E>(key, ch, L, p.k, out_row, hist, wtot, res);
       continue;
     }
 
@@ -430,7 +645,8 @@ __global__ void __launch_bounds__(BLOCK) topk_split_kernel(Params p) {
       row_barrier(&ws->bar, ++nbar * nwg, err);
       for (int i = tid; i < nb; i += BLOCK) hist[i] = g_load(&gh[i]);
       __syncthreads();
-      find_bucket<BLOCK>(hist, nb, need, lds_scan, res);
+      if (tid < kWave) find_bucket_wave(hist, nb, need, res);
+      __syncthreads();
       const uint32_t b = res[0], gt = res[1];
       cnt = res[2];
       need -= gt;
@@ -448,15 +664,13 @@ __global__ void __launch_bounds__(BLOCK) topk_split_kernel(Params p) {
     if (!use_cand) {
       // The prefix alone decides the set; publish counts for the output offsets.
       uint32_t n = 0;
-      with_pred(pf, ib, rmask, [&](const auto& pred) {
-        regs([&](uint32_t kk, int32_t j) { n += pred.ge(kk, j) ? 1u : 0u; });
-      });
-      const uint32_t total = block_sum<BLOCK>(n, lds_scan);
+      with_pred(pf, ib, rmask, [&](const auto& pred) { n = count_ge<BLOCK, E>(key, ch, pred); });
+      const uint32_t total = block_sum<BLOCK>(n, wtot);
       if (tid == 0) g_store(&ws->wg_count[g], total);
       row_barrier(&ws->bar, ++nbar * nwg, err);
       uint32_t part = 0;
       for (int i = tid; i < g; i += BLOCK) part += g_load(&ws->wg_count[i]);
-      off = block_sum<BLOCK>(part, lds_scan);
+      off = block_sum<BLOCK>(part, wtot);
     } else {
       // Entries above the bucket are taken; the bucket's entries go to the
       // row's candidate list, which every workgroup then finishes locally.
@@ -467,16 +681,20 @@ __global__ void __launch_bounds__(BLOCK) topk_split_kernel(Params p) {
           n_cand += pred.eq(kk, j) ? 1u : 0u;
         });
       });
-      uint32_t v[2] = {n_sel - n_cand, n_cand}, tot[2];
-      block_inclusive_sum<BLOCK, 2>(v, tot, lds_scan);
+      const uint32_t above = block_sum<BLOCK>(n_sel - n_cand, wtot);
+      const uint32_t cw = wave_sum(n_cand);
+      const uint32_t wave_base = wave_offset<BLOCK>(cw, wtot);
+      uint32_t ctot = 0;
+#pragma unroll
+      for (int i = 0; i < BLOCK / kWave; ++i) ctot += wtot[i];
       if (tid == 0) {
-        res[3] = tot[1] ? __hip_atomic_fetch_add(&ws->cand_count, tot[1], __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT)
-                        : 0u;
-        g_store(&ws->wg_count[g], tot[0]);
+        res[3] = ctot ? __hip_atomic_fetch_add(&ws->cand_count, ctot, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)
+                      : 0u;
+        g_store(&ws->wg_count[g], above);
       }
       __syncthreads();
-      uint32_t pos = res[3] + v[1] - n_cand;
+      uint32_t pos = res[3] + wave_base + wave_inclusive_sum(n_cand) - n_cand;
       with_pred(pr, ib, rmask, [&](const auto& pred) {
         regs([&](uint32_t kk, int32_t j) {
           if (pred.eq(kk, j)) {
@@ -490,7 +708,7 @@ __global__ void __launch_bounds__(BLOCK) topk_split_kernel(Params p) {
       const int nc = static_cast<int>(cnt);
       for (int i = tid; i < nc; i += BLOCK) cand[i] = g_load64(&ws->cand[i]);
       __syncthreads();
-      pf = rounds_local<BLOCK>(ListSource<BLOCK>{cand, nc}, pr, need, ib, hist, lds_scan, res);
+      pf = rounds_local<BLOCK>(ListSource<BLOCK>{cand, nc}, pr, need, ib, hist, res);
       for (int i = tid; i < Gr; i += BLOCK) csel[i] = 0;
       __syncthreads();
       with_pred(pf, ib, rmask, [&](const auto& pred) {
@@ -504,9 +722,9 @@ __global__ void __launch_bounds__(BLOCK) topk_split_kernel(Params p) {
       __syncthreads();
       uint32_t part = 0;
       for (int i = tid; i < g; i += BLOCK) part += g_load(&ws->wg_count[i]) + csel[i];
-      off = block_sum<BLOCK>(part, lds_scan);
+      off = block_sum<BLOCK>(part, wtot);
     }
-    emit_ordered<BLOCK, E>(key, ch, pf, ib, out_row, off, static_cast<uint32_t>(p.k), lds_scan);
+    emit_ordered<BLOCK, E>(key, ch, pf, ib, out_row, off, static_cast<uint32_t>(p.k), wtot);
 
     // Leave the row; the last workgroup out returns its workspace to zero.
     // Every read of the row's shared data happened before this arrival.
@@ -540,8 +758,8 @@ __global__ void debug_keys_kernel(const float* in, uint32_t* out, int64_t n) {
 // ---------------------------------------------------------------------------
 // Host side: planning and launch.
 // ---------------------------------------------------------------------------
-enum Kind { kLocal256x16, kLocal512x16, kLocal1024x16, kLocal1024x32, kSplit1024x16, kNumKinds };
-constexpr int kLargestLocal = kLocal1024x32;
+enum Kind { kRow256x16, kRow512x16, kRow512x32, kRow512x64, kSplit1024x16, kNumKinds };
+constexpr int kLargestLocal = kRow512x64;
 
 struct KindInfo {
   int block, e;
@@ -550,10 +768,10 @@ struct KindInfo {
 };
 
 const KindInfo kKinds[kNumKinds] = {
-    {256, 16, false, reinterpret_cast<const void*>(&topk_local_kernel<256, 16>)},
-    {512, 16, false, reinterpret_cast<const void*>(&topk_local_kernel<512, 16>)},
-    {1024, 16, false, reinterpret_cast<const void*>(&topk_local_kernel<1024, 16>)},
-    {1024, 32, false, reinterpret_cast<const void*>(&topk_local_kernel<1024, 32>)},
+    {256, 16, false, reinterpret_cast<const void*>(&topk_row_kernel<256, 16>)},
+    {512, 16, false, reinterpret_cast<const void*>(&topk_row_kernel<512, 16>)},
+    {512, 32, false, reinterpret_cast<const void*>(&topk_row_kernel<512, 32>)},
+    {512, 64, false, reinterpret_cast<const void*>(&topk_row_kernel<512, 64>)},
     {1024, 16, true, reinterpret_cast<const void*>(&topk_split_kernel<1024, 16>)},
 };
 
@@ -581,6 +799,7 @@ hipError_t device_info(DeviceInfo* out) {
     if (d.status == hipSuccess)
       d.status = hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.split_per_cu, kKinds[kSplit1024x16].fn,
                                                               kKinds[kSplit1024x16].block, 0);
+
     g_dev[dev] = d;
   });
   *out = g_dev[dev];
@@ -588,7 +807,7 @@ hipError_t device_info(DeviceInfo* out) {
 }
 
 struct Plan {
-  int kind = kLocal256x16;
+  int kind = kRow256x16;
   int64_t chunk = 0;
   int G = 1;
   int rows_per_iter = 0;
@@ -616,12 +835,13 @@ int make_plan(int64_t num_rows, int64_t row_stride, int32_t k, int path, int chu
             (need > 8192 && num_rows < 2 * static_cast<int64_t>(dev.cus));
   }
   if (!split) {
-    int kind = kLocal256x16;
+    int kind = kRow256x16;
     while (cap_of(kind) < need) ++kind;
     pl->kind = kind;
     pl->chunk = cap_of(kind);
     pl->G = 1;
     pl->grid = num_rows;
+
     pl->rows_per_iter = static_cast<int>(num_rows);
     pl->ws_bytes = 0;
     return MI_TOPK_OK;

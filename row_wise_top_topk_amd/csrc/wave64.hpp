@@ -34,6 +34,11 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
   return v + add;
 }
 
+// Sum over the lanes of one wavefront (every lane gets it).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_inclusive_sum(v)), 63));
+}
+
 // LDS words block_inclusive_sum<BLOCK, NV> needs.
 template <int BLOCK, int NV>
 constexpr int scan_lds_words() {
