@@ -579,8 +579,10 @@ __device__ __forceinline__ void select_chunk_whole_row(const uint32_t (&key)[E],
   emit_ordered<BLOCK, E>(key, ch, pf, ib, out_row, 0u, kk, wtot);
 }
 
+// Two 512-thread workgroups per CU, so that up to 512 chunks are co-resident.
 template <int BLOCK, int E>
-__global__ void __launch_bounds__(BLOCK) topk_split_kernel(Params p) {
+__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+topk_split_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[kFirstBins];
   __shared__ uint64_t cand[kCandCap];
   __shared__ uint32_t csel[kMaxChunks];
@@ -758,7 +760,7 @@ __global__ void debug_keys_kernel(const float* in, uint32_t* out, int64_t n) {
 // ---------------------------------------------------------------------------
 // Host side: planning and launch.
 // ---------------------------------------------------------------------------
-enum Kind { kRow256x16, kRow512x16, kRow512x32, kRow512x64, kSplit1024x16, kNumKinds };
+enum Kind { kRow256x16, kRow512x16, kRow512x32, kRow512x64, kSplit512x32, kNumKinds };
 constexpr int kLargestLocal = kRow512x64;
 
 struct KindInfo {
@@ -772,7 +774,7 @@ const KindInfo kKinds[kNumKinds] = {
     {512, 16, false, reinterpret_cast<const void*>(&topk_row_kernel<512, 16>)},
     {512, 32, false, reinterpret_cast<const void*>(&topk_row_kernel<512, 32>)},
     {512, 64, false, reinterpret_cast<const void*>(&topk_row_kernel<512, 64>)},
-    {1024, 16, true, reinterpret_cast<const void*>(&topk_split_kernel<1024, 16>)},
+    {512, 32, true, reinterpret_cast<const void*>(&topk_split_kernel<512, 32>)},
 };
 
 struct DeviceInfo {
@@ -797,8 +799,8 @@ hipError_t device_info(DeviceInfo* out) {
     if (d.status == hipSuccess)
       d.status = hipDeviceGetAttribute(&d.coop, hipDeviceAttributeCooperativeLaunch, dev);
     if (d.status == hipSuccess)
-      d.status = hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.split_per_cu, kKinds[kSplit1024x16].fn,
-                                                              kKinds[kSplit1024x16].block, 0);
+      d.status = hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.split_per_cu, kKinds[kSplit512x32].fn,
+                                                              kKinds[kSplit512x32].block, 0);
 
     g_dev[dev] = d;
   });
@@ -847,7 +849,7 @@ int make_plan(int64_t num_rows, int64_t row_stride, int32_t k, int path, int chu
     return MI_TOPK_OK;
   }
   if (!dev.coop || dev.split_per_cu < 1) return MI_TOPK_ELAUNCH;
-  const int64_t cap = cap_of(kSplit1024x16);
+  const int64_t cap = cap_of(kSplit512x32);
   const int64_t max_res = static_cast<int64_t>(dev.split_per_cu) * dev.cus;
   const int64_t g_min = (need + cap - 1) / cap;
   int64_t G;
@@ -863,7 +865,7 @@ int make_plan(int64_t num_rows, int64_t row_stride, int32_t k, int path, int chu
   G = (need + chunk - 1) / chunk;
   if (G > kMaxChunks || G > max_res) return MI_TOPK_ETOOLONG;
   const int64_t rows_per_iter = std::min<int64_t>(num_rows, max_res / G);
-  pl->kind = kSplit1024x16;
+  pl->kind = kSplit512x32;
   pl->chunk = chunk;
   pl->G = static_cast<int>(G);
   pl->rows_per_iter = static_cast<int>(rows_per_iter);
