@@ -459,7 +459,8 @@ __device__ __forceinline__ void select_row(uint32_t (&raw)[E], const Chunk& ch, 
   const uint32_t rmask = (1u << ib) - 1u;
   const uint32_t kk = static_cast<uint32_t>(k);
   bool done = false;
-  if (L >= 4 * k) {
+  const bool sampled = L >= 4 * k;
+  if (sampled) {
     const uint32_t lb = sample_bound<BLOCK, E>(raw, L, k, lds);
     const uint32_t cw = lb > 0x80000000u ? filter_wave<BLOCK, E, true>(raw, ch, lb, lds)
                                          : filter_wave<BLOCK, E, false>(raw, ch, lb, lds);
@@ -518,6 +519,9 @@ __device__ __forceinline__ void select_row(uint32_t (&raw)[E], const Chunk& ch, 
     __syncthreads();  // LDS is reused below
   }
   if (!done) {
+    // the row is read again rather than kept in registers through the list
+    // phase, which would otherwise spill
+    if (sampled) load_raw<BLOCK, E>(raw, ch);
     keys_in_place<BLOCK, E>(raw, ch);
     const Prefix pf =
         rounds_local<BLOCK>(RegSource<BLOCK, E>{raw, ch}, Prefix{0, 0u, 0u}, kk, ib, lds.hist, lds.res);
