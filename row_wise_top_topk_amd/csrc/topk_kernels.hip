@@ -554,6 +554,343 @@ topk_row_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// Streaming row kernel: one workgroup per row, the row streamed through
+// registers instead of held in them.
+//
+// Wavefront w owns the contiguous stretch [w*S, (w+1)*S) of the row's span
+// (S = 64*NP elements) and reads it in chunks of 16 positions (lane l's
+// position u is element w*S + u*64 + l, so each load instruction reads 256
+// consecutive bytes), alternating between two 16-word register buffers so
+// that the next chunk is in flight while the current one is filtered.  The
+// sample that fixes the filter bound is read first (one word at the start of
+// each quarter of the stretch), and its histogram search runs while the
+// first two chunks arrive.  Each wavefront then filters its own stretch into
+// its own LDS region, in column order, with no workgroup barrier until the
+// stretch is done.  80 registers and a 48 KB LDS footprint (the histogram
+// shares memory with the list) let three workgroups share a CU.
+//
+// Rows that the sample does not settle (fewer than k entries pass, or a
+// region overflows), rows shorter than 4k, and rows too short to be worth
+// sampling are selected exactly by radix rounds that read the row again from
+// memory (or, for a row of at most 16 positions per thread, from registers).
+// ---------------------------------------------------------------------------
+constexpr int kChunkPos = 16;     // positions per chunk, per thread
+constexpr int kStreamRegion = 768;  // list entries per wavefront
+
+// List entry i of wavefront w: raw bits at list[w*kStreamRegion + i], column
+// at list[kListCols + w*kStreamRegion + i] (one address, two constant offsets).
+template <int BLOCK>
+struct __attribute__((aligned(16))) StreamLds {
+  static constexpr int kListCols = (BLOCK / kWave) * kStreamRegion;
+  union {
+    uint32_t hist[kFirstBins];
+    uint32_t list[2 * kListCols];
+  } u;
+  uint32_t wtot[BLOCK / kWave];
+  uint32_t res[4];
+};
+
+// The row as read from memory in the streaming layout (NP positions per
+// thread); entries outside the row carry key 0.
+template <int BLOCK, int NP>
+struct StreamGeom {
+  __amdgpu_buffer_rsrc_t rsrc;
+  int llo, lhi;
+  int32_t jbase;
+
+  static constexpr int kStretch = kWave * NP;
+  static constexpr int kChunks = NP / kChunkPos;
+
+  __device__ __forceinline__ StreamGeom(const Chunk& ch)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(ch.base), 0, ch.lhi * 4,
+                                               0x00020000)),
+        llo(ch.llo), lhi(ch.lhi), jbase(ch.jbase) {}
+
+  // first element of this wavefront's chunk c (uniform)
+  __device__ __forceinline__ int chunk_first(int c) const {
+    return static_cast<int>(wave_id()) * kStretch + c * (kChunkPos * kWave);
+  }
+  __device__ __forceinline__ bool chunk_live(int c) const { return chunk_first(c) < lhi; }
+
+  // this thread's element at position 0 of chunk c
+  __device__ __forceinline__ int elem(int c) const {
+    int e = chunk_first(c) + static_cast<int>(__lane_id());
+    asm volatile("" : "+v"(e));
+    return e;
+  }
+
+  // Issues the loads of chunk c (positions past lhi read zeros, no memory access).
+  __device__ __forceinline__ void load(uint32_t (&buf)[kChunkPos], int c) const {
+    const int e = elem(c);
+#pragma unroll
+    for (int u = 0; u < kChunkPos; ++u)
+      buf[u] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (e + u * kWave) * 4, 0, 0);
+  }
+
+  // True if every position of chunk c lies inside [llo, lhi) (uniform).
+  __device__ __forceinline__ bool chunk_inside(int c) const {
+    const int first = chunk_first(c);
+    return first >= llo && first + kChunkPos * kWave <= lhi;
+  }
+
+  // Calls f(u, x, e) for the chunk's positions, with x the raw bits (kKeys:
+  // the key) and `outside` in place of x for positions outside [llo, lhi).
+  // The per-lane range test is made only in chunks that hold the row's
+  // start or end (one uniform branch per chunk).
+  template <bool kKeys, class F>
+  __device__ __forceinline__ void visit(const uint32_t (&buf)[kChunkPos], int c, uint32_t outside,
+                                        F f) const {
+    const int e = elem(c);
+    if (chunk_inside(c)) {
+#pragma unroll
+      for (int u = 0; u < kChunkPos; ++u)
+        f(u, kKeys ? order_key_bits(buf[u]) : buf[u], e + u * kWave);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kChunkPos; ++u) {
+        const int eu = e + u * kWave;
+        const uint32_t x = kKeys ? order_key_bits(buf[u]) : buf[u];
+        f(u, (eu >= llo && eu < lhi) ? x : outside, eu);
+      }
+    }
+  }
+
+  // (key, column) source over the whole row, read from memory chunk by chunk.
+  template <class F>
+  __device__ __forceinline__ void operator()(F f) const {
+#pragma unroll 1
+    for (int c = 0; c < kChunks; ++c) {
+      if (!chunk_live(c)) break;
+      uint32_t buf[kChunkPos];
+      load(buf, c);
+      visit<true>(buf, c, 0u, [&](int, uint32_t key, int e) { f(key, jbase + e); });
+    }
+  }
+  __device__ __forceinline__ void count(const Prefix& p, int d, int ib, uint32_t rmask,
+                                        uint32_t* hist) const {
+    count_digit(*this, p, d, ib, rmask, hist);
+  }
+};
+
+// Exact selection over the row read from memory: radix rounds, then an
+// ordered emission (a counting pass for each wavefront's offset, then one
+// ballot per position).
+template <int BLOCK, int NP>
+__device__ __forceinline__ void select_stream_exact(const StreamGeom<BLOCK, NP>& g, int L, int k,
+                                                    int32_t* out_row, StreamLds<BLOCK>& lds) {
+  const int ib = index_bits(L);
+  const uint32_t rmask = (1u << ib) - 1u;
+  const uint32_t kk = static_cast<uint32_t>(k);
+  const Prefix pf = rounds_local<BLOCK>(g, Prefix{0, 0u, 0u}, kk, ib, lds.u.hist, lds.res);
+  with_pred(pf, ib, rmask, [&](const auto& pred) {
+    uint32_t n = 0;
+    g([&](uint32_t key, int32_t j) { n += pred.ge(key, j) ? 1u : 0u; });
+    uint32_t pos_wave = wave_offset<BLOCK>(wave_sum(n), lds.wtot);
+#pragma unroll 1
+    for (int c = 0; c < StreamGeom<BLOCK, NP>::kChunks; ++c) {
+      if (!g.chunk_live(c)) break;
+      uint32_t buf[kChunkPos];
+      g.load(buf, c);
+      g.template visit<true>(buf, c, 0u, [&](int, uint32_t key, int e) {
+        const int32_t j = g.jbase + e;
+        const bool sel = pred.ge(key, j);
+        const uint64_t m = __ballot(sel);
+        const uint32_t pos = pos_wave + lanes_below(m);
+        if (sel && pos < kk) out_row[pos] = j;
+        pos_wave += static_cast<uint32_t>(__popcll(m));
+      });
+    }
+  });
+}
+
+// Filters one chunk into this wavefront's LDS region; cnt counts every
+// entry that passed.  A position's hits are stored only if all of them fit
+// (a uniform test), so a region that overflows ends with cnt above its size.
+template <int BLOCK, int NP, bool kPositiveBound>
+__device__ __forceinline__ void filter_chunk(const StreamGeom<BLOCK, NP>& g,
+                                             const uint32_t (&buf)[kChunkPos], int c, uint32_t lb,
+                                             uint32_t* region, uint32_t& cnt) {
+  constexpr int kCols = StreamLds<BLOCK>::kListCols;
+  const uint32_t ulim = 0u - lb;
+  const int32_t slim = static_cast<int32_t>(lb & 0x7FFFFFFFu);
+  const int32_t j0 = g.jbase + g.elem(c);
+  g.template visit<false>(buf, c, kOutsideBits, [&](int u, uint32_t x, int) {
+    const bool hit = kPositiveBound ? static_cast<int32_t>(x) >= slim : x <= ulim;
+    const uint64_t m = __ballot(hit);
+    const uint32_t n = static_cast<uint32_t>(__popcll(m));
+    if (cnt + n <= static_cast<uint32_t>(kStreamRegion)) {
+      if (hit) {
+        const uint32_t pos = __builtin_amdgcn_mbcnt_hi(
+            static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), cnt));
+        region[pos] = x;
+        region[kCols + pos] = static_cast<uint32_t>(j0 + u * kWave);
+      }
+    }
+    cnt += n;
+  });
+}
+
+// Streams the wavefront's stretch: chunk c+2 is loaded into the buffer that
+// chunk c has just been filtered from.  The first two chunks were issued by
+// the caller.
+template <int BLOCK, int NP, bool kPositiveBound>
+__device__ __forceinline__ uint32_t filter_stream(const StreamGeom<BLOCK, NP>& g,
+                                                  uint32_t (&a)[kChunkPos],
+                                                  uint32_t (&b)[kChunkPos], uint32_t lb,
+                                                  StreamLds<BLOCK>& lds) {
+  constexpr int NCH = StreamGeom<BLOCK, NP>::kChunks;
+  uint32_t* region = lds.u.list + wave_id() * kStreamRegion;
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (!g.chunk_live(c)) break;
+    uint32_t(&buf)[kChunkPos] = (c & 1) ? b : a;
+    filter_chunk<BLOCK, NP, kPositiveBound>(g, buf, c, lb, region, cnt);
+    if (c + 2 < NCH && g.chunk_live(c + 2)) g.load(buf, c + 2);
+  }
+  return cnt;
+}
+
+template <int BLOCK, int NP>
+__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(6)))
+topk_stream_kernel(Params p) {
+  constexpr int NW = BLOCK / kWave;
+  __shared__ StreamLds<BLOCK> lds;
+  const int64_t row = blockIdx.x;
+  const int L = row_length(p, row);
+  int32_t* out_row = p.out + row * static_cast<int64_t>(p.k);
+  if (L <= p.k) {
+    write_trivial(out_row, L, p.k, BLOCK);
+    return;
+  }
+  const float* row_ptr = p.logits + row * p.row_stride;
+  const int head = static_cast<int>((reinterpret_cast<uintptr_t>(row_ptr) >> 2) & 3u);
+  const Chunk ch = make_chunk(row_ptr, head, 0, head, head + L);
+  const int ib = index_bits(L);
+  const uint32_t rmask = (1u << ib) - 1u;
+  const uint32_t kk = static_cast<uint32_t>(p.k);
+  const int tid = threadIdx.x;
+
+  if (ch.lhi <= BLOCK * kChunkPos) {
+    // the whole row in 16 registers per thread
+    uint32_t key[kChunkPos];
+    load_raw<BLOCK, kChunkPos>(key, ch);
+    keys_in_place<BLOCK, kChunkPos>(key, ch);
+    const Prefix pf = rounds_local<BLOCK>(RegSource<BLOCK, kChunkPos>{key, ch}, Prefix{0, 0u, 0u},
+                                          kk, ib, lds.u.hist, lds.res);
+    emit_ordered<BLOCK, kChunkPos>(key, ch, pf, ib, out_row, 0u, kk, lds.wtot);
+    return;
+  }
+  const StreamGeom<BLOCK, NP> g(ch);
+  if (L < 4 * p.k) {
+    select_stream_exact<BLOCK, NP>(g, L, p.k, out_row, lds);
+    return;
+  }
+
+  // sample (one word at the start of each quarter of the stretch), then the
+  // first two chunks
+  constexpr int QS = NP / 4;
+  uint32_t smp[4];
+  {
+    const int e = g.elem(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      smp[q] = __builtin_amdgcn_raw_buffer_load_b32(g.rsrc, (e + q * QS * kWave) * 4, 0, 0);
+  }
+  uint32_t a[kChunkPos], b[kChunkPos];
+  g.load(a, 0);
+  if (g.chunk_live(1)) g.load(b, 1);
+
+  for (int i = tid; i < kFirstBins; i += BLOCK) lds.u.hist[i] = 0;
+  __syncthreads();
+  {
+    const int e = g.elem(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int eq = e + q * QS * kWave;
+      const uint32_t key = order_key_bits(smp[q]);
+      if (eq >= g.llo && eq < g.lhi && key > 1u) atomicAdd(&lds.u.hist[key >> (32 - kFirstBits)], 1u);
+    }
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    if (tid == 0) lds.res[0] = 0u;
+    find_bucket_wave_nb<kFirstBins>(
+        lds.u.hist,
+        [&](uint32_t ns) {
+          return static_cast<uint32_t>((5ull * kk * ns + 4ull * L - 1) / (4ull * L)) + 8u;
+        },
+        lds.res);
+  }
+  __syncthreads();
+  uint32_t lb = lds.res[0] << (32 - kFirstBits);
+  lb = lb < 2u ? 2u : lb;
+
+  const uint32_t cw = lb > 0x80000000u ? filter_stream<BLOCK, NP, true>(g, a, b, lb, lds)
+                                       : filter_stream<BLOCK, NP, false>(g, a, b, lb, lds);
+  const uint32_t w = wave_id();
+  if (__lane_id() == 0) lds.wtot[w] = cw;
+  __syncthreads();
+  uint32_t total = 0, over = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t c = lds.wtot[i];
+    total += c;
+    over |= c > static_cast<uint32_t>(kStreamRegion) ? 1u : 0u;
+  }
+  if (over || total < kk) {
+    __syncthreads();  // wtot is reused
+    select_stream_exact<BLOCK, NP>(g, L, p.k, out_row, lds);
+    return;
+  }
+
+  // the wavefront's list in registers: lane l takes entries [l*per, l*per+per)
+  // of its region, per a multiple of 4 (16-byte LDS reads)
+  RegList lst;
+  {
+    constexpr int kCols = StreamLds<BLOCK>::kListCols;
+    const uint32_t per = (((cw + kWave - 1) / kWave) + 3u) & ~3u;
+    const uint32_t first = __lane_id() * per;
+    const uint32_t* region = lds.u.list + w * kStreamRegion;
+#pragma unroll
+    for (int q = 0; q < kListPerThread / 4; ++q) {
+      const uint32_t i0 = first + 4u * q;
+      uint4 r = make_uint4(0u, 0u, 0u, 0u), c = make_uint4(0u, 0u, 0u, 0u);
+      if (4u * q < per) {
+        r = *reinterpret_cast<const uint4*>(region + i0);
+        c = *reinterpret_cast<const uint4*>(region + kCols + i0);
+      }
+      const uint32_t rv[4] = {r.x, r.y, r.z, r.w};
+      const uint32_t cv[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bool ok = 4u * q + t < per && i0 + t < cw;
+        lst.key[4 * q + t] = ok ? order_key_bits(rv[t]) : 0u;
+        lst.col[4 * q + t] = static_cast<int32_t>(cv[t]);
+      }
+    }
+  }
+  __syncthreads();  // the list's LDS becomes the histogram
+  const Prefix pf = rounds_local<BLOCK>(lst, Prefix{0, 0u, 0u}, kk, ib, lds.u.hist, lds.res);
+  with_pred(pf, ib, rmask, [&](const auto& pred) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int u = 0; u < kListPerThread; ++u) n += pred.ge(lst.key[u], lst.col[u]) ? 1u : 0u;
+    const uint32_t incl = wave_inclusive_sum(n);
+    const uint32_t wtotal =
+        static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+    uint32_t pos = wave_offset<BLOCK>(wtotal, lds.wtot) + incl - n;
+#pragma unroll
+    for (int u = 0; u < kListPerThread; ++u) {
+      if (pred.ge(lst.key[u], lst.col[u])) {
+        if (pos < kk) out_row[pos] = lst.col[u];
+        ++pos;
+      }
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
 // Split path: G workgroups per row, merged through the row workspace.
 // ---------------------------------------------------------------------------
 
@@ -764,8 +1101,12 @@ __global__ void debug_keys_kernel(const float* in, uint32_t* out, int64_t n) {
 // ---------------------------------------------------------------------------
 // Host side: planning and launch.
 // ---------------------------------------------------------------------------
-enum Kind { kRow256x16, kRow512x16, kRow512x32, kRow512x64, kSplit512x32, kNumKinds };
-constexpr int kLargestLocal = kRow512x64;
+enum Kind { kRow256x16, kRow512x16, kRow512x32, kRow512x64, kSplit512x32, kStream512x32,
+            kStream512x64, kNumKinds };
+// One-workgroup-per-row kernels in increasing row capacity.
+constexpr int kLocalKinds[] = {kRow256x16, kRow512x16, kStream512x32, kStream512x64};
+constexpr int kNumLocalKinds = sizeof(kLocalKinds) / sizeof(kLocalKinds[0]);
+constexpr int kLargestLocal = kLocalKinds[kNumLocalKinds - 1];
 
 struct KindInfo {
   int block, e;
@@ -779,6 +1120,8 @@ const KindInfo kKinds[kNumKinds] = {
     {512, 32, false, reinterpret_cast<const void*>(&topk_row_kernel<512, 32>)},
     {512, 64, false, reinterpret_cast<const void*>(&topk_row_kernel<512, 64>)},
     {512, 32, true, reinterpret_cast<const void*>(&topk_split_kernel<512, 32>)},
+    {512, 32, false, reinterpret_cast<const void*>(&topk_stream_kernel<512, 32>)},
+    {512, 64, false, reinterpret_cast<const void*>(&topk_stream_kernel<512, 64>)},
 };
 
 struct DeviceInfo {
@@ -841,8 +1184,9 @@ int make_plan(int64_t num_rows, int64_t row_stride, int32_t k, int path, int chu
             (need > 8192 && num_rows < 2 * static_cast<int64_t>(dev.cus));
   }
   if (!split) {
-    int kind = kRow256x16;
-    while (cap_of(kind) < need) ++kind;
+    int i = 0;
+    while (cap_of(kLocalKinds[i]) < need) ++i;
+    const int kind = kLocalKinds[i];
     pl->kind = kind;
     pl->chunk = cap_of(kind);
     pl->G = 1;
