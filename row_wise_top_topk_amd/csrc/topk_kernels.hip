@@ -575,6 +575,7 @@ topk_row_kernel(Params p) {
 // memory (or, for a row of at most 16 positions per thread, from registers).
 // ---------------------------------------------------------------------------
 constexpr int kChunkPos = 16;     // positions per chunk, per thread
+constexpr int kStreamBufs = 3;    // chunks in flight per wavefront
 constexpr int kStreamRegion = 768;  // list entries per wavefront
 
 // List entry i of wavefront w: raw bits at list[w*kStreamRegion + i], column
@@ -633,25 +634,16 @@ struct StreamGeom {
     return first >= llo && first + kChunkPos * kWave <= lhi;
   }
 
-  // Calls f(u, x, e) for the chunk's positions, with x the raw bits (kKeys:
-  // the key) and `outside` in place of x for positions outside [llo, lhi).
-  // The per-lane range test is made only in chunks that hold the row's
-  // start or end (one uniform branch per chunk).
-  template <bool kKeys, class F>
-  __device__ __forceinline__ void visit(const uint32_t (&buf)[kChunkPos], int c, uint32_t outside,
-                                        F f) const {
+  // Replaces the words of positions outside [llo, lhi) by `outside`; only
+  // chunks that hold the row's start or end are touched (a uniform branch).
+  __device__ __forceinline__ void mask_edges(uint32_t (&buf)[kChunkPos], int c,
+                                             uint32_t outside) const {
+    if (chunk_inside(c)) return;
     const int e = elem(c);
-    if (chunk_inside(c)) {
 #pragma unroll
-      for (int u = 0; u < kChunkPos; ++u)
-        f(u, kKeys ? order_key_bits(buf[u]) : buf[u], e + u * kWave);
-    } else {
-#pragma unroll
-      for (int u = 0; u < kChunkPos; ++u) {
-        const int eu = e + u * kWave;
-        const uint32_t x = kKeys ? order_key_bits(buf[u]) : buf[u];
-        f(u, (eu >= llo && eu < lhi) ? x : outside, eu);
-      }
+    for (int u = 0; u < kChunkPos; ++u) {
+      const int eu = e + u * kWave;
+      buf[u] = (eu >= llo && eu < lhi) ? buf[u] : outside;
     }
   }
 
@@ -663,7 +655,12 @@ struct StreamGeom {
       if (!chunk_live(c)) break;
       uint32_t buf[kChunkPos];
       load(buf, c);
-      visit<true>(buf, c, 0u, [&](int, uint32_t key, int e) { f(key, jbase + e); });
+#pragma unroll
+      for (int u = 0; u < kChunkPos; ++u) buf[u] = order_key_bits(buf[u]);
+      mask_edges(buf, c, 0u);
+      const int32_t j0 = jbase + elem(c);
+#pragma unroll
+      for (int u = 0; u < kChunkPos; ++u) f(buf[u], j0 + u * kWave);
     }
   }
   __device__ __forceinline__ void count(const Prefix& p, int d, int ib, uint32_t rmask,
@@ -691,14 +688,19 @@ __device__ __forceinline__ void select_stream_exact(const StreamGeom<BLOCK, NP>&
       if (!g.chunk_live(c)) break;
       uint32_t buf[kChunkPos];
       g.load(buf, c);
-      g.template visit<true>(buf, c, 0u, [&](int, uint32_t key, int e) {
-        const int32_t j = g.jbase + e;
-        const bool sel = pred.ge(key, j);
+#pragma unroll
+      for (int u = 0; u < kChunkPos; ++u) buf[u] = order_key_bits(buf[u]);
+      g.mask_edges(buf, c, 0u);
+      const int32_t j0 = g.jbase + g.elem(c);
+#pragma unroll
+      for (int u = 0; u < kChunkPos; ++u) {
+        const int32_t j = j0 + u * kWave;
+        const bool sel = pred.ge(buf[u], j);
         const uint64_t m = __ballot(sel);
         const uint32_t pos = pos_wave + lanes_below(m);
         if (sel && pos < kk) out_row[pos] = j;
         pos_wave += static_cast<uint32_t>(__popcll(m));
-      });
+      }
     }
   });
 }
@@ -706,7 +708,9 @@ __device__ __forceinline__ void select_stream_exact(const StreamGeom<BLOCK, NP>&
 // Filters one chunk into this wavefront's LDS region; cnt counts every
 // entry that passed.  A position's hits are stored only if all of them fit
 // (a uniform test), so a region that overflows ends with cnt above its size.
-template <int BLOCK, int NP, bool kPositiveBound>
+// kEdge: the chunk holds the row's end; positions past it are read as
+// kOutsideBits (the buffer itself is not modified).
+template <int BLOCK, int NP, bool kPositiveBound, bool kEdge>
 __device__ __forceinline__ void filter_chunk(const StreamGeom<BLOCK, NP>& g,
                                              const uint32_t (&buf)[kChunkPos], int c, uint32_t lb,
                                              uint32_t* region, uint32_t& cnt) {
@@ -714,7 +718,9 @@ __device__ __forceinline__ void filter_chunk(const StreamGeom<BLOCK, NP>& g,
   const uint32_t ulim = 0u - lb;
   const int32_t slim = static_cast<int32_t>(lb & 0x7FFFFFFFu);
   const int32_t j0 = g.jbase + g.elem(c);
-  g.template visit<false>(buf, c, kOutsideBits, [&](int u, uint32_t x, int) {
+#pragma unroll
+  for (int u = 0; u < kChunkPos; ++u) {
+    const uint32_t x = !kEdge || j0 + u * kWave < g.jbase + g.lhi ? buf[u] : kOutsideBits;
     const bool hit = kPositiveBound ? static_cast<int32_t>(x) >= slim : x <= ulim;
     const uint64_t m = __ballot(hit);
     const uint32_t n = static_cast<uint32_t>(__popcll(m));
@@ -727,26 +733,30 @@ __device__ __forceinline__ void filter_chunk(const StreamGeom<BLOCK, NP>& g,
       }
     }
     cnt += n;
-  });
+  }
 }
 
-// Streams the wavefront's stretch: chunk c+2 is loaded into the buffer that
-// chunk c has just been filtered from.  The first two chunks were issued by
-// the caller.
+// Streams the wavefront's stretch through kStreamBufs register buffers:
+// chunk c + kStreamBufs is loaded into the buffer that chunk c has just been
+// filtered from.  The first kStreamBufs chunks were issued by the caller.
 template <int BLOCK, int NP, bool kPositiveBound>
 __device__ __forceinline__ uint32_t filter_stream(const StreamGeom<BLOCK, NP>& g,
-                                                  uint32_t (&a)[kChunkPos],
-                                                  uint32_t (&b)[kChunkPos], uint32_t lb,
-                                                  StreamLds<BLOCK>& lds) {
+                                                  uint32_t (&bufs)[kStreamBufs][kChunkPos],
+                                                  uint32_t lb, StreamLds<BLOCK>& lds) {
   constexpr int NCH = StreamGeom<BLOCK, NP>::kChunks;
   uint32_t* region = lds.u.list + wave_id() * kStreamRegion;
   uint32_t cnt = 0;
+  // the row starts at element 0, so only the chunk holding its end is partial
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    if (!g.chunk_live(c)) break;
-    uint32_t(&buf)[kChunkPos] = (c & 1) ? b : a;
-    filter_chunk<BLOCK, NP, kPositiveBound>(g, buf, c, lb, region, cnt);
-    if (c + 2 < NCH && g.chunk_live(c + 2)) g.load(buf, c + 2);
+    if (g.chunk_inside(c)) {
+      filter_chunk<BLOCK, NP, kPositiveBound, false>(g, bufs[c % kStreamBufs], c, lb, region, cnt);
+    } else if (g.chunk_live(c)) {
+      filter_chunk<BLOCK, NP, kPositiveBound, true>(g, bufs[c % kStreamBufs], c, lb, region, cnt);
+    }
+    // issued even for chunks past the row's end (they read nothing): a load
+    // behind a branch makes every later wait for the buffers conservative
+    if (c + kStreamBufs < NCH) g.load(bufs[c % kStreamBufs], c + kStreamBufs);
   }
   return cnt;
 }
@@ -764,8 +774,8 @@ topk_stream_kernel(Params p) {
     return;
   }
   const float* row_ptr = p.logits + row * p.row_stride;
-  const int head = static_cast<int>((reinterpret_cast<uintptr_t>(row_ptr) >> 2) & 3u);
-  const Chunk ch = make_chunk(row_ptr, head, 0, head, head + L);
+  // word loads need no 16-byte alignment, so the row starts at element 0
+  const Chunk ch = make_chunk(row_ptr, 0, 0, 0, L);
   const int ib = index_bits(L);
   const uint32_t rmask = (1u << ib) - 1u;
   const uint32_t kk = static_cast<uint32_t>(p.k);
@@ -797,9 +807,10 @@ topk_stream_kernel(Params p) {
     for (int q = 0; q < 4; ++q)
       smp[q] = __builtin_amdgcn_raw_buffer_load_b32(g.rsrc, (e + q * QS * kWave) * 4, 0, 0);
   }
-  uint32_t a[kChunkPos], b[kChunkPos];
-  g.load(a, 0);
-  if (g.chunk_live(1)) g.load(b, 1);
+  uint32_t bufs[kStreamBufs][kChunkPos];
+#pragma unroll
+  for (int c = 0; c < kStreamBufs; ++c)
+    if (c < StreamGeom<BLOCK, NP>::kChunks) g.load(bufs[c], c);
 
   for (int i = tid; i < kFirstBins; i += BLOCK) lds.u.hist[i] = 0;
   __syncthreads();
@@ -826,8 +837,8 @@ topk_stream_kernel(Params p) {
   uint32_t lb = lds.res[0] << (32 - kFirstBits);
   lb = lb < 2u ? 2u : lb;
 
-  const uint32_t cw = lb > 0x80000000u ? filter_stream<BLOCK, NP, true>(g, a, b, lb, lds)
-                                       : filter_stream<BLOCK, NP, false>(g, a, b, lb, lds);
+  const uint32_t cw = lb > 0x80000000u ? filter_stream<BLOCK, NP, true>(g, bufs, lb, lds)
+                                       : filter_stream<BLOCK, NP, false>(g, bufs, lb, lds);
   const uint32_t w = wave_id();
   if (__lane_id() == 0) lds.wtot[w] = cw;
   __syncthreads();
@@ -1111,17 +1122,18 @@ constexpr int kLargestLocal = kLocalKinds[kNumLocalKinds - 1];
 struct KindInfo {
   int block, e;
   bool split;
+  bool aligned;  // the kernel starts a row's span at the 16-byte boundary below it
   const void* fn;
 };
 
 const KindInfo kKinds[kNumKinds] = {
-    {256, 16, false, reinterpret_cast<const void*>(&topk_row_kernel<256, 16>)},
-    {512, 16, false, reinterpret_cast<const void*>(&topk_row_kernel<512, 16>)},
-    {512, 32, false, reinterpret_cast<const void*>(&topk_row_kernel<512, 32>)},
-    {512, 64, false, reinterpret_cast<const void*>(&topk_row_kernel<512, 64>)},
-    {512, 32, true, reinterpret_cast<const void*>(&topk_split_kernel<512, 32>)},
-    {512, 32, false, reinterpret_cast<const void*>(&topk_stream_kernel<512, 32>)},
-    {512, 64, false, reinterpret_cast<const void*>(&topk_stream_kernel<512, 64>)},
+    {256, 16, false, true, reinterpret_cast<const void*>(&topk_row_kernel<256, 16>)},
+    {512, 16, false, true, reinterpret_cast<const void*>(&topk_row_kernel<512, 16>)},
+    {512, 32, false, true, reinterpret_cast<const void*>(&topk_row_kernel<512, 32>)},
+    {512, 64, false, true, reinterpret_cast<const void*>(&topk_row_kernel<512, 64>)},
+    {512, 32, true, true, reinterpret_cast<const void*>(&topk_split_kernel<512, 32>)},
+    {512, 32, false, false, reinterpret_cast<const void*>(&topk_stream_kernel<512, 32>)},
+    {512, 64, false, false, reinterpret_cast<const void*>(&topk_stream_kernel<512, 64>)},
 };
 
 struct DeviceInfo {
@@ -1166,26 +1178,32 @@ struct Plan {
 
 int64_t cap_of(int kind) { return static_cast<int64_t>(kKinds[kind].block) * kKinds[kind].e; }
 
+// Elements a row can span in `kind`'s layout: the stride, plus the
+// misalignment below a 16-byte boundary for kernels that align row starts.
+int64_t span_of(int kind, int64_t row_stride, int head_max) {
+  return row_stride + (kKinds[kind].aligned ? head_max : 0);
+}
+
 // head_max: largest misalignment (in elements) of a row start below a 16-byte
 // boundary: 0 when logits is 16-byte aligned and row_stride % 4 == 0, else 3.
 int make_plan(int64_t num_rows, int64_t row_stride, int32_t k, int path, int chunks, int head_max,
               const DeviceInfo& dev, Plan* pl) {
   (void)k;
   const int64_t need = row_stride + head_max;  // elements a row can span from its aligned start
+  const bool fits_local = span_of(kLargestLocal, row_stride, head_max) <= cap_of(kLargestLocal);
   bool split;
   if (path == MI_TOPK_PATH_LOCAL) {
-    if (need > cap_of(kLargestLocal)) return MI_TOPK_ETOOLONG;
+    if (!fits_local) return MI_TOPK_ETOOLONG;
     split = false;
   } else if (path == MI_TOPK_PATH_SPLIT) {
     split = true;
   } else {
     // Few long rows cannot fill the device with one workgroup each.
-    split = need > cap_of(kLargestLocal) ||
-            (need > 8192 && num_rows < 2 * static_cast<int64_t>(dev.cus));
+    split = !fits_local || (row_stride > 8192 && num_rows < 2 * static_cast<int64_t>(dev.cus));
   }
   if (!split) {
     int i = 0;
-    while (cap_of(kLocalKinds[i]) < need) ++i;
+    while (cap_of(kLocalKinds[i]) < span_of(kLocalKinds[i], row_stride, head_max)) ++i;
     const int kind = kLocalKinds[i];
     pl->kind = kind;
     pl->chunk = cap_of(kind);
