@@ -59,7 +59,7 @@ struct Prefix {
 
 __device__ __forceinline__ int digit_bits(int bits, int ib) {
   if (bits == 0) return kFirstBits;
-  if (bits < 32) return kNextBits;
+  if (bits < 32) return 32 - bits < kNextBits ? 32 - bits : kNextBits;  // digits end at the key's end
   const int left = 32 + ib - bits;
   return left < kNextBits ? left : kNextBits;
 }
@@ -307,6 +307,37 @@ __device__ __forceinline__ Prefix rounds_local(const Src& src, Prefix p, uint32_
     if (cnt == need) break;
   }
   return p;
+}
+
+// Radix rounds for entries whose keys all lie in [lo, hi] (entries outside
+// the row carry key 0).  The first round histograms the key bits just below
+// the ones every key in [lo, hi] shares: the shift s is the smallest that
+// puts hi >> s and lo >> s fewer than kFirstBins apart, and bin i counts keys
+// with key >> s == (lo >> s) + i, so its bucket is an ordinary key prefix of
+// 32 - s bits.  When the keys are confined to a narrow range (a filtered
+// list), that one round resolves as many bits as two or three full-range
+// digits and spreads the entries over many bins.  Later rounds continue with
+// rounds_local.  Returns the final prefix.
+template <int BLOCK, class Src>
+__device__ __forceinline__ Prefix rounds_window(const Src& src, uint32_t lo, uint32_t hi,
+                                                uint32_t need, int ib, uint32_t* hist,
+                                                uint32_t* res) {
+  int s = 0;
+  while ((hi >> s) - (lo >> s) >= static_cast<uint32_t>(kFirstBins)) ++s;
+  const uint32_t base = lo >> s;
+  for (int i = threadIdx.x; i < kFirstBins; i += BLOCK) hist[i] = 0;
+  __syncthreads();
+  src([&](uint32_t key, int32_t) {
+    if (key != 0u) atomicAdd(&hist[(key >> s) - base], 1u);
+  });
+  __syncthreads();
+  if (threadIdx.x < kWave) find_bucket_wave_nb<kFirstBins>(hist, [need](uint32_t) { return need; }, res);
+  __syncthreads();
+  const uint32_t b = res[0], gt = res[1], cnt = res[2];
+  need -= gt;
+  const Prefix p{32 - s, base + b, 0u};
+  if (cnt == need) return p;
+  return rounds_local<BLOCK>(src, p, need, ib, hist, res);
 }
 
 }  // namespace mitopk

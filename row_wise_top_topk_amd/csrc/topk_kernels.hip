@@ -841,6 +841,7 @@ topk_stream_kernel(Params p) {
                                        : filter_stream<BLOCK, NP, false>(g, bufs, lb, lds);
   const uint32_t w = wave_id();
   if (__lane_id() == 0) lds.wtot[w] = cw;
+  if (tid == 0) lds.res[3] = 0u;  // the list's largest key, below
   __syncthreads();
   uint32_t total = 0, over = 0;
 #pragma unroll
@@ -880,9 +881,16 @@ topk_stream_kernel(Params p) {
         lst.col[4 * q + t] = static_cast<int32_t>(cv[t]);
       }
     }
+    uint32_t mx = 0;
+#pragma unroll
+    for (int u = 0; u < kListPerThread; ++u) mx = max(mx, lst.key[u]);
+    mx = wave_max(mx);
+    if (__lane_id() == 0) atomicMax(&lds.res[3], mx);
   }
   __syncthreads();  // the list's LDS becomes the histogram
-  const Prefix pf = rounds_local<BLOCK>(lst, Prefix{0, 0u, 0u}, kk, ib, lds.u.hist, lds.res);
+  // every listed key lies in [lb, largest]
+  const uint32_t kmax = lds.res[3];
+  const Prefix pf = rounds_window<BLOCK>(lst, lb, kmax, kk, ib, lds.u.hist, lds.res);
   with_pred(pf, ib, rmask, [&](const auto& pred) {
     uint32_t n = 0;
 #pragma unroll
