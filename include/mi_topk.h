@@ -100,13 +100,20 @@ const char* topk_status_string(int status);
  *   MI_TOPK_PATH_LOCAL  one workgroup per row holds the whole row on chip
  *                       (rows up to 32768 entries);
  *   MI_TOPK_PATH_SPLIT  `chunks` workgroups per row (0 = automatic) hold one
- *                       chunk each and merge their histograms in workspace.
+ *                       chunk each and merge their histograms in workspace
+ *                       (a cooperative launch; any k);
+ *   MI_TOPK_PATH_CHUNKS one workgroup per 16384-entry chunk of a row; each
+ *                       publishes the entries above a bound estimated from
+ *                       its own chunk, and the row's last workgroup selects
+ *                       among them (an ordinary launch; k <= 4096, `chunks`
+ *                       ignored).
  * topk_workspace_size_path() and topk_indices_path() otherwise behave like
  * topk_workspace_size() and topk_indices().
  */
 #define MI_TOPK_PATH_AUTO 0
 #define MI_TOPK_PATH_LOCAL 1
 #define MI_TOPK_PATH_SPLIT 2
+#define MI_TOPK_PATH_CHUNKS 3
 
 size_t topk_workspace_size_path(int64_t num_rows, int64_t row_stride, int32_t k,
                                 int32_t path, int32_t chunks);

@@ -15,13 +15,13 @@ import threading
 import torch
 
 __all__ = [
-    "PATH_AUTO", "PATH_LOCAL", "PATH_SPLIT",
+    "PATH_AUTO", "PATH_LOCAL", "PATH_SPLIT", "PATH_CHUNKS",
     "library_path", "load_library", "topk_indices", "workspace_size",
     "plan_describe", "debug_keys", "workspace_error", "status_string",
 ]
 
-PATH_AUTO, PATH_LOCAL, PATH_SPLIT = 0, 1, 2
-_PATHS = {"auto": PATH_AUTO, "local": PATH_LOCAL, "split": PATH_SPLIT}
+PATH_AUTO, PATH_LOCAL, PATH_SPLIT, PATH_CHUNKS = 0, 1, 2, 3
+_PATHS = {"auto": PATH_AUTO, "local": PATH_LOCAL, "split": PATH_SPLIT, "chunks": PATH_CHUNKS}
 MAX_K = 1 << 24
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

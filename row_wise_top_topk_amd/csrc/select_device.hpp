@@ -155,6 +155,56 @@ __device__ __forceinline__ void count_digit(ForEach for_each, const Prefix& p, i
   }
 }
 
+// hist[bin] += 1 for the lanes with `take`, as one atomic when every such
+// lane of the wavefront has the same bin (the rows of a tied or constant
+// input, where per-lane atomics to one address would serialise), else one
+// per lane.  Every lane of the wavefront must call it.
+__device__ __forceinline__ void hist_add_wave(uint32_t* hist, uint32_t bin, bool take) {
+  const uint64_t tm = __ballot(take);
+  if (tm == 0) return;
+  const int first = __ffsll(static_cast<unsigned long long>(tm)) - 1;
+  const uint32_t b0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), first));
+  const uint64_t same = __ballot(take && bin == b0);
+  if (same == tm) {
+    if (static_cast<int>(__lane_id()) == first) atomicAdd(&hist[b0], static_cast<uint32_t>(__popcll(tm)));
+  } else if (take) {
+    atomicAdd(&hist[bin], 1u);
+  }
+}
+
+// count_digit with wavefront-aggregated increments (hist_add_wave); for_each
+// must call f for the same number of entries on every lane.
+template <class ForEach>
+__device__ __forceinline__ void count_digit_agg(ForEach for_each, const Prefix& p, int d, int ib,
+                                                uint32_t rmask, uint32_t* hist) {
+  const uint32_t dmask = (1u << d) - 1u;
+  if (p.bits == 0) {
+    const int sh = 32 - d;
+    for_each([&](uint32_t key, int32_t) { hist_add_wave(hist, key >> sh, key != 0u); });
+  } else if (p.bits < 32) {
+    const int sh = 32 - p.bits;
+    const int dsh = sh - d;
+    const uint32_t kp = p.kp;
+    if (kp != 0u) {
+      for_each([&](uint32_t key, int32_t) {
+        hist_add_wave(hist, (key >> dsh) & dmask, (key >> sh) == kp);
+      });
+    } else {
+      for_each([&](uint32_t key, int32_t) {
+        hist_add_wave(hist, (key >> dsh) & dmask, key != 0u && (key >> sh) == 0u);
+      });
+    }
+  } else {
+    const int ish = ib - (p.bits - 32);
+    const int dsh = ish - d;
+    const uint32_t T = p.kp, ip = p.ip;
+    for_each([&](uint32_t key, int32_t j) {
+      const uint32_t ridx = rmask - static_cast<uint32_t>(j);
+      hist_add_wave(hist, (ridx >> dsh) & dmask, key == T && (ridx >> ish) == ip);
+    });
+  }
+}
+
 // Finds the bucket b holding the need-th largest entry of a histogram of nb
 // bins (nb a power of two): the largest b with sum(hist[b..nb)) >= need.
 // Thread t owns a group of adjacent bins counted from the top; a workgroup

@@ -1104,11 +1104,401 @@ topk_split_kernel(Params p) {
         uint32_t* gh = ws->hist + hist_offset(r);
         for (int i = tid; i < nbins; i += BLOCK) g_store(&gh[i], 0u);
       }
+      // published counts and candidates too: the workspace is left all zero,
+      // whichever path uses it next
+      for (int i = tid; i < Gr; i += BLOCK) g_store(&ws->wg_count[i], 0u);
+      if (use_cand) {
+        const uint32_t nc = cnt < static_cast<uint32_t>(kCandCap) ? cnt : kCandCap;
+        for (uint32_t i = tid; i < nc; i += BLOCK) g_store64(&ws->cand[i], 0ull);
+      }
       if (tid == 0) g_store(&ws->cand_count, 0u);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (tid == 0) g_store(&ws->bar, 0u);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunked path: G workgroups per row and no grid-wide synchronisation.
+//
+// Each workgroup holds one chunk of a row (BLOCK*E entries) in registers and
+// estimates, from a sample of its own chunk, a bound below which no entry of
+// the row's top k is expected: with ns sample entries of a chunk of a row of
+// length L, k*ns/L of them are expected at or above the row's threshold, and
+// the bound is the first-digit bin edge where the sample's count from the top
+// reaches ceil(2 k ns / L) + 12, far beyond that expectation.  The chunk's
+// entries at or above its bound go to the row's workspace in column order,
+// with the chunk's count and bound.  The last workgroup of the row to arrive
+// (a device-scope counter, which it then resets) gathers the chunks'
+// candidates into registers and selects the top k among them.  The result is
+// the row's top k whenever every chunk's bound lies at or below the smallest
+// selected key: an entry a chunk did not publish is below that chunk's bound,
+// hence below every selected entry.  This is checked; a row that fails it,
+// or whose candidates overflow, is selected exactly by the same workgroup
+// with radix rounds that stream the row from memory.
+// ---------------------------------------------------------------------------
+constexpr int kChunkCap = 4096;       // candidates one chunk may publish
+constexpr int kUnionPerThread = 16;   // candidates per thread in the final selection
+constexpr int kChunkSamples = 16;     // sample positions per thread
+
+// Row r's block in the workspace (after the header) starts at
+// r * chunk_row_bytes(G): a 256-byte head whose word 0 counts the row's
+// arrived workgroups, then count[G] and bound[G] (rounded to 256 bytes), then
+// the candidates, G slots of kChunkCap entries (key << 32 | column).
+__host__ __device__ constexpr size_t chunk_row_bytes(int G) {
+  return 256 + ((8 * static_cast<size_t>(G) + 255) / 256) * 256 +
+         static_cast<size_t>(G) * kChunkCap * 8;
+}
+
+// The union of the chunks' candidates in registers: thread t holds entries
+// t, t + BLOCK, t + 2*BLOCK, ... of the union (which is in column order);
+// unused entries have key 0.
+struct UnionList {
+  uint32_t key[kUnionPerThread];
+  int32_t col[kUnionPerThread];
+  template <class F>
+  __device__ __forceinline__ void operator()(F f) const {
+#pragma unroll
+    for (int u = 0; u < kUnionPerThread; ++u) f(key[u], col[u]);
+  }
+  __device__ __forceinline__ void count(const Prefix& p, int d, int ib, uint32_t rmask,
+                                        uint32_t* hist) const {
+    count_digit(*this, p, d, ib, rmask, hist);
+  }
+};
+
+// A whole row read from memory in blocks of BLOCK*16 entries (position u of
+// thread (w, l) in block b is entry b*BLOCK*16 + w*1024 + u*64 + l, so the
+// visiting order is column order); entries past the row carry key 0.
+template <int BLOCK>
+struct RowStream {
+  __amdgpu_buffer_rsrc_t rsrc;
+  int L;
+  static constexpr int kBlockElems = BLOCK * kChunkPos;
+  static constexpr int kRowBufs = 3;  // blocks in flight
+
+  __device__ __forceinline__ RowStream(const float* row, int len)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, len * 4, 0x00020000)),
+        L(len) {}
+
+  __device__ __forceinline__ int elem0(int base) const {
+    int e = base + static_cast<int>(wave_id()) * (kWave * kChunkPos) +
+            static_cast<int>(__lane_id());
+    asm volatile("" : "+v"(e));
+    return e;
+  }
+  // Loads block `base` (positions past the row read nothing).
+  __device__ __forceinline__ void load(uint32_t (&buf)[kChunkPos], int e0) const {
+#pragma unroll
+    for (int u = 0; u < kChunkPos; ++u)
+      buf[u] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (e0 + u * kWave) * 4, 0, 0);
+  }
+  __device__ __forceinline__ void keys(uint32_t (&buf)[kChunkPos], int e0) const {
+#pragma unroll
+    for (int u = 0; u < kChunkPos; ++u)
+      buf[u] = e0 + u * kWave < L ? order_key_bits(buf[u]) : 0u;
+  }
+  // Visits the row's blocks in order, block b+kRowBufs-1 loading while
+  // block b is visited: visit(buf, e0) gets a block's keys.  The loads are
+  // issued unconditionally (past the row they read nothing), so the
+  // compiler's waits stay exact.
+  template <class V>
+  __device__ __forceinline__ void blocks(V visit) const {
+    uint32_t buf[kRowBufs][kChunkPos];
+#pragma unroll
+    for (int i = 0; i < kRowBufs - 1; ++i) load(buf[i], elem0(i * kBlockElems));
+#pragma unroll 1
+    for (int base = 0; base < L; base += kRowBufs * kBlockElems) {
+#pragma unroll
+      for (int i = 0; i < kRowBufs; ++i) {
+        const int bb = base + i * kBlockElems;
+        load(buf[(i + kRowBufs - 1) % kRowBufs], elem0(bb + (kRowBufs - 1) * kBlockElems));
+        const int e0 = elem0(bb);
+        keys(buf[i], e0);
+        visit(buf[i], e0);
+      }
+    }
+  }
+  template <class F>
+  __device__ __forceinline__ void operator()(F f) const {
+    blocks([&](const uint32_t (&buf)[kChunkPos], int e0) {
+#pragma unroll
+      for (int u = 0; u < kChunkPos; ++u) f(buf[u], e0 + u * kWave);
+    });
+  }
+  __device__ __forceinline__ void count(const Prefix& p, int d, int ib, uint32_t rmask,
+                                        uint32_t* hist) const {
+    count_digit_agg(*this, p, d, ib, rmask, hist);
+  }
+};
+
+// Exact selection of a whole row streamed from memory by one workgroup:
+// radix rounds, then, block by block, an ordered emission.
+template <int BLOCK>
+__device__ __forceinline__ void select_row_streamed(const float* row, int L, int k, int32_t* out_row,
+                                                 uint32_t* hist, uint32_t* wtot, uint32_t* res) {
+  constexpr int NW = BLOCK / kWave;
+  const RowStream<BLOCK> src(row, L);
+  const int ib = index_bits(L);
+  const uint32_t rmask = (1u << ib) - 1u;
+  const uint32_t kk = static_cast<uint32_t>(k);
+  const Prefix pf = rounds_local<BLOCK>(src, Prefix{0, 0u, 0u}, kk, ib, hist, res);
+  with_pred(pf, ib, rmask, [&](const auto& pred) {
+    uint32_t out_base = 0;
+    src.blocks([&](const uint32_t (&buf)[kChunkPos], int e0) {
+      uint32_t n = 0;
+#pragma unroll
+      for (int u = 0; u < kChunkPos; ++u) n += pred.ge(buf[u], e0 + u * kWave) ? 1u : 0u;
+      uint32_t pos = out_base + wave_offset<BLOCK>(wave_sum(n), wtot);
+      uint32_t block_total = 0;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) block_total += wtot[i];
+#pragma unroll
+      for (int u = 0; u < kChunkPos; ++u) {
+        const int32_t j = e0 + u * kWave;
+        const bool sel = pred.ge(buf[u], j);
+        const uint64_t m = __ballot(sel);
+        const uint32_t at = pos + lanes_below(m);
+        if (sel && at < kk) out_row[at] = j;
+        pos += static_cast<uint32_t>(__popcll(m));
+      }
+      out_base += block_total;
+      __syncthreads();  // wtot is reused
+    });
+  });
+}
+
+template <int BLOCK, int E>
+__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+topk_chunks_kernel(Params p) {
+  constexpr int NW = BLOCK / kWave;
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kFirstBins];
+  __shared__ uint32_t coff[kMaxChunks + 1];
+  __shared__ uint32_t wtot[NW];
+  __shared__ uint32_t res[12];
+  const int tid = threadIdx.x;
+  const int G = p.G;
+  const int64_t row = blockIdx.x / G;
+  const int g = static_cast<int>(blockIdx.x % G);
+  const int L = row_length(p, row);
+  int32_t* out_row = p.out + row * static_cast<int64_t>(p.k);
+  if (L <= p.k) {
+    if (g == 0) write_trivial(out_row, L, p.k, BLOCK);
+    return;
+  }
+  const int chunk = BLOCK * E;
+  const int Gr = (L + chunk - 1) / chunk;
+  if (g >= Gr) return;
+  const float* row_ptr = p.logits + row * p.row_stride;
+  const int64_t cbase = static_cast<int64_t>(g) * chunk;
+  const int clen = static_cast<int>(L - cbase < chunk ? L - cbase : chunk);
+  const Chunk ch = make_chunk(row_ptr, 0, cbase, 0, clen);
+  const uint32_t kk = static_cast<uint32_t>(p.k);
+  const int ib = index_bits(L);
+  const uint32_t rmask = (1u << ib) - 1u;
+  uint32_t raw[E];
+  load_raw<BLOCK, E>(raw, ch);
+  if (Gr == 1) {
+    keys_in_place<BLOCK, E>(raw, ch);
+    select_chunk_whole_row<BLOCK, E>(raw, ch, L, p.k, out_row, hist, wtot, res);
+    return;
+  }
+
+  uint8_t* rb = p.ws + kWsHeader + static_cast<size_t>(row) * chunk_row_bytes(G);
+  uint32_t* arrived = reinterpret_cast<uint32_t*>(rb);
+  uint32_t* counts = reinterpret_cast<uint32_t*>(rb + 256);
+  uint32_t* bounds = counts + G;
+  uint64_t* cand = reinterpret_cast<uint64_t*>(rb + 256 + ((8 * static_cast<size_t>(G) + 255) / 256) * 256);
+
+  // sample: kChunkSamples positions per thread, spread over its E positions
+  for (int i = tid; i < kFirstBins; i += BLOCK) hist[i] = 0;
+  if (tid == 0) res[0] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kChunkSamples; ++q) {
+    const uint32_t key = order_key_bits(raw[q * (E / kChunkSamples)]);
+    hist_add_wave(hist, key >> (32 - kFirstBits), key > 1u);  // kOutsideBits: key 1
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    find_bucket_wave_nb<kFirstBins>(
+        hist,
+        [&](uint32_t ns) {
+          return static_cast<uint32_t>((2ull * kk * ns + L - 1) / static_cast<uint64_t>(L)) + 12u;
+        },
+        res);
+  }
+  __syncthreads();
+  uint32_t lb = res[0] << (32 - kFirstBits);
+  lb = lb < 2u ? 2u : lb;
+
+  // publish the chunk's entries with key >= lb, in column order
+  const int32_t j0 = ch.jbase + thread_elem0<E>();
+  uint32_t n = 0;
+#pragma unroll
+  for (int u = 0; u < E; ++u) n += order_key_bits(raw[u]) >= lb ? 1u : 0u;
+  uint32_t pos = wave_offset<BLOCK>(wave_sum(n), wtot);
+  uint32_t total = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) total += wtot[i];
+  uint64_t* my = cand + static_cast<size_t>(g) * kChunkCap;
+#pragma unroll
+  for (int u = 0; u < E; ++u) {
+    const uint32_t key = order_key_bits(raw[u]);
+    const bool hit = key >= lb;
+    const uint64_t m = __ballot(hit);
+    const uint32_t at = pos + lanes_below(m);
+    if (hit && at < static_cast<uint32_t>(kChunkCap))
+      g_store64(&my[at], (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(j0 + u * kWave));
+    pos += static_cast<uint32_t>(__popcll(m));
+  }
+  if (tid == 0) {
+    g_store(&counts[g], total);
+    g_store(&bounds[g], lb);
+  }
+  // arrive; every store above has completed before the counter moves
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    res[4] = old == static_cast<uint32_t>(Gr) - 1u ? 1u : 0u;
+  }
+  __syncthreads();
+  if (res[4] == 0u) return;
+
+  // ---- the row's last workgroup: select among the chunks' candidates ----
+  if (tid == 0) g_store(arrived, 0u);  // every workgroup of the row has arrived
+  if (tid < kWave) {
+    // offsets of the chunks' candidates in the union, total, bounds
+    uint32_t run = 0, lo = 0xFFFFFFFFu, hi = 0u, bad = 0u;
+    for (int b0 = 0; b0 < Gr; b0 += kWave) {
+      const int c = b0 + tid;
+      const uint32_t cnt = c < Gr ? g_load(&counts[c]) : 0u;
+      const uint32_t bnd = c < Gr ? g_load(&bounds[c]) : 0u;
+      const uint32_t incl = wave_inclusive_sum(cnt);
+      if (c < Gr) coff[c] = run + incl - cnt;
+      run += static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+      if (c < Gr) {
+        lo = bnd < lo ? bnd : lo;
+        hi = bnd > hi ? bnd : hi;
+        bad |= cnt > static_cast<uint32_t>(kChunkCap) ? 1u : 0u;
+      }
+    }
+    hi = wave_max(hi);
+    lo = ~wave_max(~lo);
+    bad = wave_max(bad);
+    if (tid == 0) {
+      coff[Gr] = run;
+      res[5] = run;
+      res[6] = lo;
+      res[7] = hi;
+      res[8] = bad;
+      res[3] = 0u;
+    }
+  }
+  __syncthreads();
+  const uint32_t utotal = res[5], min_lb = res[6], max_lb = res[7];
+  const bool exact_ok = res[8] == 0u && utotal >= kk &&
+                  utotal <= static_cast<uint32_t>(BLOCK * kUnionPerThread);
+  bool done = false;
+  if (exact_ok) {
+    // union entry i = s*BLOCK + t goes to thread t, slot s (consecutive
+    // threads read consecutive candidates).  A map from union entry to chunk
+    // (16-bit, in the histogram's LDS; wavefront w fills the chunks
+    // c = w mod NW) lets all of a thread's loads issue back to back.
+    uint16_t* chunk_of = reinterpret_cast<uint16_t*>(hist);
+    for (int c = static_cast<int>(wave_id()); c < Gr; c += NW)
+      for (uint32_t i = coff[c] + __lane_id(); i < coff[c + 1]; i += kWave)
+        chunk_of[i] = static_cast<uint16_t>(c);
+    __syncthreads();
+    UnionList un;
+    {
+      const uint32_t t = static_cast<uint32_t>(tid);
+      uint32_t at[kUnionPerThread];
+      uint64_t e[kUnionPerThread];
+#pragma unroll
+      for (int sl = 0; sl < kUnionPerThread; ++sl) {
+        const uint32_t i = static_cast<uint32_t>(sl * BLOCK) + t;
+        const bool ok = i < utotal;
+        const uint32_t c = ok ? chunk_of[i] : 0u;
+        at[sl] = ok ? c * static_cast<uint32_t>(kChunkCap) + (i - coff[c]) : 0u;
+      }
+#pragma unroll
+      for (int sl = 0; sl < kUnionPerThread; ++sl) e[sl] = g_load64(&cand[at[sl]]);
+      uint32_t mx = 0;
+#pragma unroll
+      for (int sl = 0; sl < kUnionPerThread; ++sl) {
+        const bool ok = static_cast<uint32_t>(sl * BLOCK) + t < utotal;
+        un.key[sl] = ok ? static_cast<uint32_t>(e[sl] >> 32) : 0u;
+        un.col[sl] = static_cast<int32_t>(static_cast<uint32_t>(e[sl]));
+        mx = max(mx, un.key[sl]);
+      }
+      // the candidates are in registers: return their slots to zero (other
+      // paths may use the workspace next)
+#pragma unroll
+      for (int sl = 0; sl < kUnionPerThread; ++sl)
+        if (un.key[sl] != 0u) g_store64(&cand[at[sl]], 0ull);
+      mx = wave_max(mx);
+      if (__lane_id() == 0) atomicMax(&res[3], mx);
+    }
+    __syncthreads();
+    const uint32_t kmax = res[3];
+    const Prefix pf = rounds_window<BLOCK>(un, min_lb, kmax, kk, ib, hist, res);
+    // every selected key is at least the selected bucket's lower edge
+    const uint32_t edge = pf.bits >= 32 ? pf.kp : (pf.kp << (32 - pf.bits));
+    if (edge >= max_lb) {
+      // ordered emission: the union's order is (slot, thread); per slot and
+      // wavefront counts give each selected entry its rank
+      uint32_t* wslot = hist;                            // [slot][wave] counts
+      uint32_t* pre = hist + kUnionPerThread * NW;       // [slot][wave] offsets
+      const uint32_t w = wave_id();
+      with_pred(pf, ib, rmask, [&](const auto& pred) {
+        uint64_t m[kUnionPerThread];
+#pragma unroll
+        for (int sl = 0; sl < kUnionPerThread; ++sl) {
+          m[sl] = __ballot(pred.ge(un.key[sl], un.col[sl]));
+          if (__lane_id() == 0) wslot[sl * NW + w] = static_cast<uint32_t>(__popcll(m[sl]));
+        }
+        __syncthreads();
+        if (tid < kWave) {
+          // lane l < kUnionPerThread: slot l's total; a prefix over the lanes
+          // gives each slot's start, then every (slot, wavefront) pair its
+          // offset
+          uint32_t tot = 0;
+          if (tid < kUnionPerThread)
+            for (int i = 0; i < NW; ++i) tot += wslot[tid * NW + i];
+          const uint32_t start = wave_inclusive_sum(tot) - tot;
+          for (int q = tid; q < kUnionPerThread * NW; q += kWave) {
+            const int sl = q / NW, wv = q % NW;
+            uint32_t before = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(sl << 2, static_cast<int>(start)));
+            for (int i = 0; i < wv; ++i) before += wslot[sl * NW + i];
+            pre[q] = before;
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int sl = 0; sl < kUnionPerThread; ++sl) {
+          const uint32_t at = pre[sl * NW + w] + lanes_below(m[sl]);
+          if (((m[sl] >> __lane_id()) & 1u) && at < kk) out_row[at] = un.col[sl];
+        }
+      });
+    }
+    done = edge >= max_lb;
+    __syncthreads();
+  }
+  if (!done) select_row_streamed<BLOCK>(row_ptr, L, p.k, out_row, hist, wtot, res);
+  if (!exact_ok) {
+    for (int c = 0; c < Gr; ++c) {
+      const uint32_t cnt = coff[c + 1] - coff[c];
+      const uint32_t used = cnt < static_cast<uint32_t>(kChunkCap) ? cnt : kChunkCap;
+      for (uint32_t j = static_cast<uint32_t>(tid); j < used; j += BLOCK)
+        g_store64(&cand[static_cast<size_t>(c) * kChunkCap + j], 0ull);
+    }
+  }
+  for (int c = tid; c < Gr; c += BLOCK) {
+    g_store(&counts[c], 0u);
+    g_store(&bounds[c], 0u);
   }
 }
 
@@ -1121,27 +1511,34 @@ __global__ void debug_keys_kernel(const float* in, uint32_t* out, int64_t n) {
 // Host side: planning and launch.
 // ---------------------------------------------------------------------------
 enum Kind { kRow256x16, kRow512x16, kRow512x32, kRow512x64, kSplit512x32, kStream512x32,
-            kStream512x64, kNumKinds };
+            kStream512x64, kChunks512x32, kNumKinds };
+
+// Largest k the chunked path takes; above it the candidates of a row would
+// crowd the final selection, and the cooperative split path is used.
+constexpr int32_t kChunksMaxK = 4096;
 // One-workgroup-per-row kernels in increasing row capacity.
 constexpr int kLocalKinds[] = {kRow256x16, kRow512x16, kStream512x32, kStream512x64};
 constexpr int kNumLocalKinds = sizeof(kLocalKinds) / sizeof(kLocalKinds[0]);
 constexpr int kLargestLocal = kLocalKinds[kNumLocalKinds - 1];
 
+enum Mode { kModeRow, kModeSplit, kModeChunks };
+
 struct KindInfo {
   int block, e;
-  bool split;
+  Mode mode;     // one workgroup per row; cooperative split; chunked
   bool aligned;  // the kernel starts a row's span at the 16-byte boundary below it
   const void* fn;
 };
 
 const KindInfo kKinds[kNumKinds] = {
-    {256, 16, false, true, reinterpret_cast<const void*>(&topk_row_kernel<256, 16>)},
-    {512, 16, false, true, reinterpret_cast<const void*>(&topk_row_kernel<512, 16>)},
-    {512, 32, false, true, reinterpret_cast<const void*>(&topk_row_kernel<512, 32>)},
-    {512, 64, false, true, reinterpret_cast<const void*>(&topk_row_kernel<512, 64>)},
-    {512, 32, true, true, reinterpret_cast<const void*>(&topk_split_kernel<512, 32>)},
-    {512, 32, false, false, reinterpret_cast<const void*>(&topk_stream_kernel<512, 32>)},
-    {512, 64, false, false, reinterpret_cast<const void*>(&topk_stream_kernel<512, 64>)},
+    {256, 16, kModeRow, true, reinterpret_cast<const void*>(&topk_row_kernel<256, 16>)},
+    {512, 16, kModeRow, true, reinterpret_cast<const void*>(&topk_row_kernel<512, 16>)},
+    {512, 32, kModeRow, true, reinterpret_cast<const void*>(&topk_row_kernel<512, 32>)},
+    {512, 64, kModeRow, true, reinterpret_cast<const void*>(&topk_row_kernel<512, 64>)},
+    {512, 32, kModeSplit, true, reinterpret_cast<const void*>(&topk_split_kernel<512, 32>)},
+    {512, 32, kModeRow, false, reinterpret_cast<const void*>(&topk_stream_kernel<512, 32>)},
+    {512, 64, kModeRow, false, reinterpret_cast<const void*>(&topk_stream_kernel<512, 64>)},
+    {512, 32, kModeChunks, false, reinterpret_cast<const void*>(&topk_chunks_kernel<512, 32>)},
 };
 
 struct DeviceInfo {
@@ -1196,14 +1593,13 @@ int64_t span_of(int kind, int64_t row_stride, int head_max) {
 // boundary: 0 when logits is 16-byte aligned and row_stride % 4 == 0, else 3.
 int make_plan(int64_t num_rows, int64_t row_stride, int32_t k, int path, int chunks, int head_max,
               const DeviceInfo& dev, Plan* pl) {
-  (void)k;
   const int64_t need = row_stride + head_max;  // elements a row can span from its aligned start
   const bool fits_local = span_of(kLargestLocal, row_stride, head_max) <= cap_of(kLargestLocal);
   bool split;
   if (path == MI_TOPK_PATH_LOCAL) {
     if (!fits_local) return MI_TOPK_ETOOLONG;
     split = false;
-  } else if (path == MI_TOPK_PATH_SPLIT) {
+  } else if (path == MI_TOPK_PATH_SPLIT || path == MI_TOPK_PATH_CHUNKS) {
     split = true;
   } else {
     // Few long rows cannot fill the device with one workgroup each.
@@ -1220,6 +1616,22 @@ int make_plan(int64_t num_rows, int64_t row_stride, int32_t k, int path, int chu
 
     pl->rows_per_iter = static_cast<int>(num_rows);
     pl->ws_bytes = 0;
+    return MI_TOPK_OK;
+  }
+  if (path == MI_TOPK_PATH_CHUNKS || (path == MI_TOPK_PATH_AUTO && k <= kChunksMaxK)) {
+    // G chunks of BLOCK*E entries per row, one workgroup each, rows starting
+    // at element 0; the last workgroup of a row selects among the chunks'
+    // candidates
+    const int64_t cap = cap_of(kChunks512x32);
+    const int64_t G = (row_stride + cap - 1) / cap;
+    if (G > kMaxChunks || num_rows * G > INT32_MAX) return MI_TOPK_ETOOLONG;
+    if (k > kChunksMaxK) return MI_TOPK_EINVAL;
+    pl->kind = kChunks512x32;
+    pl->chunk = cap;
+    pl->G = static_cast<int>(G);
+    pl->rows_per_iter = static_cast<int>(num_rows);
+    pl->grid = num_rows * G;
+    pl->ws_bytes = kWsHeader + static_cast<size_t>(num_rows) * chunk_row_bytes(static_cast<int>(G));
     return MI_TOPK_OK;
   }
   if (!dev.coop || dev.split_per_cu < 1) return MI_TOPK_ELAUNCH;
@@ -1268,7 +1680,7 @@ int launch(const Plan& pl, Params prm, hipStream_t stream) {
   const KindInfo& ki = kKinds[pl.kind];
   void* args[] = {&prm};
   hipError_t e;
-  if (ki.split) {
+  if (ki.mode == kModeSplit) {
     e = hipLaunchCooperativeKernel(ki.fn, dim3(static_cast<unsigned>(pl.grid)), dim3(ki.block), args, 0,
                                    stream);
   } else {
@@ -1282,7 +1694,7 @@ int topk_impl(const float* logits, int64_t row_stride, const int32_t* lengths, i
               hipStream_t stream) {
   int st = check_shape(num_rows, row_stride, k);
   if (st != MI_TOPK_OK) return st;
-  if (path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_SPLIT || chunks < 0) return MI_TOPK_EINVAL;
+  if (path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_CHUNKS || chunks < 0) return MI_TOPK_EINVAL;
   if (num_rows == 0) return MI_TOPK_OK;
   if (!logits || !lengths || !out) return MI_TOPK_EINVAL;
   if ((reinterpret_cast<uintptr_t>(logits) & 3u) || (reinterpret_cast<uintptr_t>(lengths) & 3u) ||
@@ -1320,7 +1732,7 @@ MI_TOPK_EXPORT size_t topk_workspace_size(int64_t num_rows, int64_t row_stride, 
 
 MI_TOPK_EXPORT size_t topk_workspace_size_path(int64_t num_rows, int64_t row_stride, int32_t k,
                                                int32_t path, int32_t chunks) {
-  if (path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_SPLIT || chunks < 0) return 0;
+  if (path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_CHUNKS || chunks < 0) return 0;
   return workspace_size_impl(num_rows, row_stride, k, path, chunks);
 }
 
@@ -1343,7 +1755,7 @@ MI_TOPK_EXPORT int topk_plan_describe(int64_t num_rows, int64_t row_stride, int3
                                       int32_t chunks, int64_t* info) {
   int st = check_shape(num_rows, row_stride, k);
   if (st != MI_TOPK_OK) return st;
-  if (!info || path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_SPLIT || chunks < 0) return MI_TOPK_EINVAL;
+  if (!info || path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_CHUNKS || chunks < 0) return MI_TOPK_EINVAL;
   DeviceInfo dev;
   if (device_info(&dev) != hipSuccess) return MI_TOPK_ELAUNCH;
   Plan pl;
@@ -1351,7 +1763,9 @@ MI_TOPK_EXPORT int topk_plan_describe(int64_t num_rows, int64_t row_stride, int3
   st = make_plan(num_rows, row_stride, k, path, chunks, head_max, dev, &pl);
   if (st != MI_TOPK_OK) return st;
   const KindInfo& ki = kKinds[pl.kind];
-  info[0] = ki.split ? MI_TOPK_PATH_SPLIT : MI_TOPK_PATH_LOCAL;
+  info[0] = ki.mode == kModeSplit ? MI_TOPK_PATH_SPLIT
+            : ki.mode == kModeChunks ? MI_TOPK_PATH_CHUNKS
+                                     : MI_TOPK_PATH_LOCAL;
   info[1] = ki.block;
   info[2] = ki.e;
   info[3] = pl.chunk;

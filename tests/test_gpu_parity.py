@@ -43,7 +43,7 @@ def test_named_workloads_match_oracle(name):
 def test_misaligned_base_and_odd_stride(offset, stride):
     lengths = [1, 5, 511, 512, 513, stride - 3, stride, stride - 1]
     w = workloads.make_custom(len(lengths), stride, lengths, 512, seed=stride + offset, kind="normal")
-    for path in ("auto", "split"):
+    for path in ("auto", "split", "chunks"):
         got = run_gpu(w, path=path, offset=offset)
         assert_parity(w, got, label=f"{path} off={offset} stride={stride}")
 
@@ -54,7 +54,8 @@ def test_local_and_split_agree_with_oracle(kind):
     lengths = [20000, 19999, 17, 2048, 2049, 12345, 4096, 16384]
     w = workloads.make_custom(len(lengths), stride, lengths, 2048, seed=7, kind=kind)
     ref = expected(w)
-    for path, chunks in (("local", 0), ("split", 0), ("split", 2), ("split", 3), ("split", 7)):
+    for path, chunks in (("local", 0), ("split", 0), ("split", 2), ("split", 3), ("split", 7),
+                         ("chunks", 0)):
         got = run_gpu(w, path=path, chunks=chunks)
         assert np.array_equal(got, ref), f"{kind} {path} chunks={chunks}"
 
@@ -67,6 +68,9 @@ def test_k_sweep_in_one_process(k):
     assert_parity(w, got, label=f"k={k}")
     got = run_gpu(w, path="split", chunks=4)
     assert_parity(w, got, label=f"k={k} split")
+    if k <= 4096:
+        got = run_gpu(w, path="chunks")
+        assert_parity(w, got, label=f"k={k} chunks")
 
 
 def test_lengths_are_clamped_and_empty_rows_padded():
@@ -99,7 +103,7 @@ def test_special_values():
     rows.append(sub.astype(np.uint32).view(np.float32))
     flat = torch.from_numpy(np.concatenate(rows))
     w = workloads.Workload("special", flat, stride, torch.full((4,), stride, dtype=torch.int32), 4, 300)
-    for path in ("local", "split"):
+    for path in ("local", "split", "chunks"):
         assert_parity(w, run_gpu(w, path=path), label=f"special {path}")
 
 
@@ -128,3 +132,43 @@ def test_workspace_reuse_across_calls():
         assert np.array_equal(out.cpu().numpy(), ref)
     torch.cuda.synchronize()
     assert mt.workspace_error(ws) == 0
+
+
+@pytest.mark.parametrize("kind", ["outliers", "normal", "bf16", "equal", "ramp", "levels"])
+def test_chunks_long_rows(kind):
+    # rows of 19 chunks: sampled bounds, the last-workgroup merge, and (for
+    # tied or ordered rows) the streamed exact fallback; lengths cut chunks
+    # at odd places
+    stride = 300032
+    lengths = [300000, 300032, 16385, 45000, 131071]
+    w = workloads.make_custom(len(lengths), stride, lengths, 2048, seed=21, kind=kind)
+    ref = expected(w)
+    for path in ("auto", "chunks"):
+        got = run_gpu(w, path=path)
+        assert np.array_equal(got, ref), f"{kind} {path}"
+
+
+def test_chunks_path_is_chosen_for_long_rows():
+    plan = mt.plan_describe(8, 900096, 2048)
+    assert plan["path"] == mt.PATH_CHUNKS
+    assert plan["chunks_per_row"] == (900096 + 16383) // 16384
+    assert mt.plan_describe(8, 900096, 5000)["path"] == mt.PATH_SPLIT
+
+
+def test_paths_share_one_workspace():
+    # every path returns the workspace to zero, so the paths can alternate
+    # on one buffer; tied rows send the chunked path through its fallback
+    stride, k = 60000, 1024
+    lengths = [60000, 59999, 20000, 16385, 3, 40000]
+    w = workloads.make_custom(len(lengths), stride, lengths, k, seed=31, kind="bf16")
+    w2 = workloads.make_custom(len(lengths), stride, lengths, k, seed=32, kind="levels")
+    need = max(mt.workspace_size(len(lengths), stride, k, path=p) for p in ("split", "chunks"))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    for wl in (w, w2):
+        logits, lens = device_view(wl)
+        ref = expected(wl)
+        for path in ("chunks", "split", "chunks", "chunks", "split"):
+            out = mt.topk_indices(logits, lens, k, workspace=ws, path=path)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), ref), path
+            assert int(ws.count_nonzero()) == 0, path
