@@ -1,9 +1,11 @@
 """Benchmark: batched, row-wise, stride-correct top-k index selection on one GPU.
 
 One step = one call of the library's top-k over the whole batch (all rows),
-with the inputs already resident in HBM.  Two copies of the input are used in
-turn so that consecutive steps do not find the previous step's data in the
-256 MB last-level cache.  Prints one JSON line.
+with the inputs already resident in HBM.  Copies of the input are used in
+turn, enough that more than 600 MB (twice the L2 caches plus the 256 MB
+last-level cache) is touched between two uses of one copy, so that no step
+finds its input in a cache (2 copies for the prefill batch, 21 for the
+long-context batch).  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload prefill]
 """
@@ -101,6 +103,16 @@ def gpu_env() -> dict:
     return env
 
 
+COLD_BYTES = 600e6   # bytes touched between two uses of one input copy
+MAX_COPIES = 64
+
+
+def input_copies(w) -> int:
+    """Copies of the input that keep every step cold in the caches."""
+    footprint = 4.0 * w.num_rows * w.row_stride
+    return int(min(MAX_COPIES, max(2, -(-COLD_BYTES // footprint))))
+
+
 def time_workload(w, steps: int, warmup: int, copies: int = 2):
     import row_wise_top_topk_amd as mt
     dev = torch.device("cuda:0")
@@ -172,7 +184,8 @@ def main() -> None:
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_rows)   # before the GPU is initialised (fork pool)
 
-    total_ms, per_launch, wall = time_workload(w, args.steps, args.warmup)
+    copies = input_copies(w)
+    total_ms, per_launch, wall = time_workload(w, args.steps, args.warmup, copies=copies)
     ms_per_step = total_ms / args.steps
     alg_bytes = w.algorithmic_bytes()
     avg_launch_ms = float(np.mean(per_launch))
@@ -200,7 +213,8 @@ def main() -> None:
         "data": "synthetic",
         "config": {"workload": DESCRIPTIONS[args.workload], "rows": w.num_rows,
                    "row_stride": w.row_stride, "k": w.k, "valid_elements": w.valid_elements,
-                   "algorithmic_bytes": alg_bytes, "parallelism": "single GPU"},
+                   "algorithmic_bytes": alg_bytes, "input_copies": copies,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "cpu_baseline": cpu,
@@ -213,10 +227,11 @@ def main() -> None:
     }
     if args.secondary and args.secondary != args.workload:
         w2 = workloads.make(args.secondary)
-        t2, pl2, _ = time_workload(w2, args.steps, args.warmup, copies=12)
+        c2 = input_copies(w2)
+        t2, pl2, _ = time_workload(w2, args.steps, args.warmup, copies=c2)
         b2 = w2.algorithmic_bytes()
         m2 = float(np.mean(pl2))
-        result["secondary"] = {"workload": DESCRIPTIONS[args.secondary],
+        result["secondary"] = {"workload": DESCRIPTIONS[args.secondary], "input_copies": c2,
                                "launch_us_mean": m2 * 1e3,
                                "launch_us_p50": float(np.percentile(pl2, 50)) * 1e3,
                                "rows_per_s": w2.num_rows / (t2 / args.steps * 1e-3),

@@ -1343,15 +1343,16 @@ topk_chunks_kernel(Params p) {
 #pragma unroll
   for (int i = 0; i < NW; ++i) total += wtot[i];
   uint64_t* my = cand + static_cast<size_t>(g) * kChunkCap;
+  if (total <= static_cast<uint32_t>(kChunkCap)) {  // else the row falls back: publish the count only
 #pragma unroll
-  for (int u = 0; u < E; ++u) {
-    const uint32_t key = order_key_bits(raw[u]);
-    const bool hit = key >= lb;
-    const uint64_t m = __ballot(hit);
-    const uint32_t at = pos + lanes_below(m);
-    if (hit && at < static_cast<uint32_t>(kChunkCap))
-      g_store64(&my[at], (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(j0 + u * kWave));
-    pos += static_cast<uint32_t>(__popcll(m));
+    for (int u = 0; u < E; ++u) {
+      const uint32_t key = order_key_bits(raw[u]);
+      const bool hit = key >= lb;
+      const uint64_t m = __ballot(hit);
+      const uint32_t at = pos + lanes_below(m);
+      if (hit) g_store64(&my[at], (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(j0 + u * kWave));
+      pos += static_cast<uint32_t>(__popcll(m));
+    }
   }
   if (tid == 0) {
     g_store(&counts[g], total);
@@ -1491,7 +1492,7 @@ topk_chunks_kernel(Params p) {
   if (!exact_ok) {
     for (int c = 0; c < Gr; ++c) {
       const uint32_t cnt = coff[c + 1] - coff[c];
-      const uint32_t used = cnt < static_cast<uint32_t>(kChunkCap) ? cnt : kChunkCap;
+      const uint32_t used = cnt <= static_cast<uint32_t>(kChunkCap) ? cnt : 0u;  // see the publish
       for (uint32_t j = static_cast<uint32_t>(tid); j < used; j += BLOCK)
         g_store64(&cand[static_cast<size_t>(c) * kChunkCap + j], 0ull);
     }
