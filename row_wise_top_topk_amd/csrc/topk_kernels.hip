@@ -1127,7 +1127,7 @@ topk_split_kernel(Params p) {
 // the row's top k is expected: with ns sample entries of a chunk of a row of
 // length L, k*ns/L of them are expected at or above the row's threshold, and
 // the bound is the first-digit bin edge where the sample's count from the top
-// reaches ceil(2 k ns / L) + 12, far beyond that expectation.  The chunk's
+// reaches ceil(3 k ns / 2L) + 16, far beyond that expectation.  The chunk's
 // entries at or above its bound go to the row's workspace in column order,
 // with the chunk's count and bound.  The last workgroup of the row to arrive
 // (a device-scope counter, which it then resets) gathers the chunks'
@@ -1325,7 +1325,7 @@ topk_chunks_kernel(Params p) {
     find_bucket_wave_nb<kFirstBins>(
         hist,
         [&](uint32_t ns) {
-          return static_cast<uint32_t>((2ull * kk * ns + L - 1) / static_cast<uint64_t>(L)) + 12u;
+          return static_cast<uint32_t>((3ull * kk * ns + 2ull * L - 1) / (2ull * L)) + 16u;
         },
         res);
   }
