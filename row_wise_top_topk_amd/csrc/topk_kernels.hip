@@ -1511,8 +1511,8 @@ __global__ void debug_keys_kernel(const float* in, uint32_t* out, int64_t n) {
 // ---------------------------------------------------------------------------
 // Host side: planning and launch.
 // ---------------------------------------------------------------------------
-enum Kind { kRow256x16, kRow512x16, kRow512x32, kRow512x64, kSplit512x32, kStream512x32,
-            kStream512x64, kChunks512x32, kNumKinds };
+enum Kind { kRow256x16, kRow512x16, kSplit512x32, kStream512x32, kStream512x64, kChunks512x32,
+            kNumKinds };
 
 // Largest k the chunked path takes; above it the candidates of a row would
 // crowd the final selection, and the cooperative split path is used.
@@ -1534,8 +1534,6 @@ struct KindInfo {
 const KindInfo kKinds[kNumKinds] = {
     {256, 16, kModeRow, true, reinterpret_cast<const void*>(&topk_row_kernel<256, 16>)},
     {512, 16, kModeRow, true, reinterpret_cast<const void*>(&topk_row_kernel<512, 16>)},
-    {512, 32, kModeRow, true, reinterpret_cast<const void*>(&topk_row_kernel<512, 32>)},
-    {512, 64, kModeRow, true, reinterpret_cast<const void*>(&topk_row_kernel<512, 64>)},
     {512, 32, kModeSplit, true, reinterpret_cast<const void*>(&topk_split_kernel<512, 32>)},
     {512, 32, kModeRow, false, reinterpret_cast<const void*>(&topk_stream_kernel<512, 32>)},
     {512, 64, kModeRow, false, reinterpret_cast<const void*>(&topk_stream_kernel<512, 64>)},

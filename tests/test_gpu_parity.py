@@ -172,3 +172,22 @@ def test_paths_share_one_workspace():
             torch.cuda.synchronize()
             assert np.array_equal(out.cpu().numpy(), ref), path
             assert int(ws.count_nonzero()) == 0, path
+
+
+def test_chunks_cluster_in_one_chunk():
+    # one chunk holds a block of 3000 equal high values: its count exceeds the
+    # last workgroup's fixed window, so the union is gathered through the
+    # chunk offsets, and the threshold value is tied 3000 ways
+    rows, stride, k = 4, 100000, 2048
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((rows, stride)).astype(np.float32)
+    for r in range(rows):
+        start = 16384 + 1000 * r
+        x[r, start:start + 3000] = 5.0
+    flat = torch.from_numpy(x.reshape(-1))
+    lengths = torch.tensor([stride, stride - 7, 99000, 70001], dtype=torch.int32)
+    w = workloads.Workload("cluster", flat, stride, lengths, rows, k)
+    ref = expected(w)
+    for path in ("chunks", "split"):
+        got = run_gpu(w, path=path)
+        assert np.array_equal(got, ref), path
