@@ -85,6 +85,11 @@ __device__ __forceinline__ uint64_t g_load64(uint64_t* p) {
 __device__ __forceinline__ void g_store64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Cache-policy operand of the buffer intrinsics that gives sc1, the policy of
+// the device-scope relaxed atomic loads and stores above on gfx950.
+constexpr int kCoherent = 16;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Barrier among the workgroups of one row (`target` arrivals in all).
 // Every access to data shared between the row's workgroups (histograms,
@@ -1137,6 +1142,15 @@ topk_split_kernel(Params p) {
 // hence below every selected entry.  This is checked; a row that fails it,
 // or whose candidates overflow, is selected exactly by the same workgroup
 // with radix rounds that stream the row from memory.
+//
+// A chunk publishes keys and column offsets in two lists.  The final
+// workgroup reads chunk c's keys into union entries [c*W, c*W + count_c),
+// W = 4 * floor(BLOCK*kUnionPerThread / 4G) (whole 16-byte groups): the
+// slots past a chunk's count hold zero (key 0, never selected), so these
+// loads need no counts and go out with the loads of the counts and bounds.
+// When some chunk published more than W, the union is packed instead, by
+// offsets from the counts.  The selected columns are staged in LDS at their
+// ranks and written out in order.
 // ---------------------------------------------------------------------------
 constexpr int kChunkCap = 4096;       // candidates one chunk may publish
 constexpr int kUnionPerThread = 16;   // candidates per thread in the final selection
@@ -1145,22 +1159,29 @@ constexpr int kChunkSamples = 16;     // sample positions per thread
 // Row r's block in the workspace (after the header) starts at
 // r * chunk_row_bytes(G): a 256-byte head whose word 0 counts the row's
 // arrived workgroups, then count[G] and bound[G] (rounded to 256 bytes), then
-// the candidates, G slots of kChunkCap entries (key << 32 | column).
+// the candidates' keys (u32, G lists of kChunkCap) and their column offsets
+// within the chunk (u16, G lists of kChunkCap).
 __host__ __device__ constexpr size_t chunk_row_bytes(int G) {
   return 256 + ((8 * static_cast<size_t>(G) + 255) / 256) * 256 +
-         static_cast<size_t>(G) * kChunkCap * 8;
+         static_cast<size_t>(G) * kChunkCap * 6;
 }
 
 // The union of the chunks' candidates in registers: thread t holds entries
 // t, t + BLOCK, t + 2*BLOCK, ... of the union (which is in column order);
-// unused entries have key 0.
+// unused entries have key 0.  An entry's column is its chunk's first column
+// plus the offset published with it.
+template <int CHUNK>
 struct UnionList {
   uint32_t key[kUnionPerThread];
-  int32_t col[kUnionPerThread];
+  uint32_t sat[kUnionPerThread];  // candidate slot: chunk << 12 | offset in the chunk's list
+  uint32_t off[kUnionPerThread];  // column offset within the chunk (loaded late)
+  __device__ __forceinline__ int32_t col(int u) const {
+    return static_cast<int32_t>((sat[u] >> 12) * static_cast<uint32_t>(CHUNK) + off[u]);
+  }
   template <class F>
   __device__ __forceinline__ void operator()(F f) const {
 #pragma unroll
-    for (int u = 0; u < kUnionPerThread; ++u) f(key[u], col[u]);
+    for (int u = 0; u < kUnionPerThread; ++u) f(key[u], col(u));
   }
   __device__ __forceinline__ void count(const Prefix& p, int d, int ib, uint32_t rmask,
                                         uint32_t* hist) const {
@@ -1275,6 +1296,8 @@ topk_chunks_kernel(Params p) {
   constexpr int NW = BLOCK / kWave;
   __shared__ __attribute__((aligned(16))) uint32_t hist[kFirstBins];
   __shared__ uint32_t coff[kMaxChunks + 1];
+  __shared__ uint16_t scol[kChunkCap];
+  __shared__ uint32_t wq[4 * NW];
   __shared__ uint32_t wtot[NW];
   __shared__ uint32_t res[12];
   const int tid = threadIdx.x;
@@ -1297,19 +1320,28 @@ topk_chunks_kernel(Params p) {
   const uint32_t kk = static_cast<uint32_t>(p.k);
   const int ib = index_bits(L);
   const uint32_t rmask = (1u << ib) - 1u;
-  uint32_t raw[E];
-  load_raw<BLOCK, E>(raw, ch);
   if (Gr == 1) {
-    keys_in_place<BLOCK, E>(raw, ch);
-    select_chunk_whole_row<BLOCK, E>(raw, ch, L, p.k, out_row, hist, wtot, res);
+    // (the chunk is loaded inside each branch: a load before it kept the
+    // registers of one branch live through the other)
+    uint32_t raw1[E];
+    load_raw<BLOCK, E>(raw1, ch);
+    keys_in_place<BLOCK, E>(raw1, ch);
+    select_chunk_whole_row<BLOCK, E>(raw1, ch, L, p.k, out_row, hist, wtot, res);
     return;
   }
+  uint32_t kv[E];
+  load_raw<BLOCK, E>(kv, ch);
+  // keys in place; positions outside the row (kOutsideBits) get key 1, below
+  // every bound and skipped by the sample
+#pragma unroll
+  for (int u = 0; u < E; ++u) kv[u] = order_key_bits(kv[u]);
 
   uint8_t* rb = p.ws + kWsHeader + static_cast<size_t>(row) * chunk_row_bytes(G);
   uint32_t* arrived = reinterpret_cast<uint32_t*>(rb);
   uint32_t* counts = reinterpret_cast<uint32_t*>(rb + 256);
   uint32_t* bounds = counts + G;
-  uint64_t* cand = reinterpret_cast<uint64_t*>(rb + 256 + ((8 * static_cast<size_t>(G) + 255) / 256) * 256);
+  uint8_t* ckeys = rb + 256 + ((8 * static_cast<size_t>(G) + 255) / 256) * 256;  // u32 [G][kChunkCap]
+  uint8_t* ccols = ckeys + static_cast<size_t>(G) * kChunkCap * 4;                 // u16 [G][kChunkCap]
 
   // sample: kChunkSamples positions per thread, spread over its E positions
   for (int i = tid; i < kFirstBins; i += BLOCK) hist[i] = 0;
@@ -1317,7 +1349,7 @@ topk_chunks_kernel(Params p) {
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < kChunkSamples; ++q) {
-    const uint32_t key = order_key_bits(raw[q * (E / kChunkSamples)]);
+    const uint32_t key = kv[q * (E / kChunkSamples)];
     hist_add_wave(hist, key >> (32 - kFirstBits), key > 1u);  // kOutsideBits: key 1
   }
   __syncthreads();
@@ -1325,33 +1357,69 @@ topk_chunks_kernel(Params p) {
     find_bucket_wave_nb<kFirstBins>(
         hist,
         [&](uint32_t ns) {
-          return static_cast<uint32_t>((3ull * kk * ns + 2ull * L - 1) / (2ull * L)) + 16u;
+          const uint32_t nd = static_cast<uint32_t>((3ull * kk * ns + 2ull * L - 1) / (2ull * L)) + 16u;
+          if (__lane_id() == 0) res[9] = nd;
+          return nd;
         },
         res);
   }
   __syncthreads();
-  uint32_t lb = res[0] << (32 - kFirstBits);
-  lb = lb < 2u ? 2u : lb;
+  // The first-digit bin holding the need-th sample is refined by the next
+  // digit, so the bound sits at that sample (to 22 bits) rather than at the
+  // bin's lower edge, which on smooth data is up to twice as many entries
+  // further down.  Bin 0 (also: too few samples) leaves the bound at 2.
+  uint32_t lb = 2u;
+  const uint32_t b0 = res[0];
+  if (b0 != 0u) {
+    const uint32_t need2 = res[9] - res[1];
+    __syncthreads();  // res and hist are reused
+    for (int i = tid; i < kNextBins; i += BLOCK) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kChunkSamples; ++q) {
+      const uint32_t key = kv[q * (E / kChunkSamples)];
+      hist_add_wave(hist, (key >> (32 - kFirstBits - kNextBits)) & (kNextBins - 1),
+                    (key >> (32 - kFirstBits)) == b0);
+    }
+    __syncthreads();
+    if (tid < kWave) find_bucket_wave_nb<kNextBins>(hist, [need2](uint32_t) { return need2; }, res);
+    __syncthreads();
+    lb = (b0 << (32 - kFirstBits)) | (res[0] << (32 - kFirstBits - kNextBits));
+  }
 
-  // publish the chunk's entries with key >= lb, in column order
-  const int32_t j0 = ch.jbase + thread_elem0<E>();
+  // publish the chunk's entries with key >= lb, in column order: staged in
+  // LDS (keys in the histogram's words, column offsets in scol), then
+  // written out by consecutive threads
   uint32_t n = 0;
 #pragma unroll
-  for (int u = 0; u < E; ++u) n += order_key_bits(raw[u]) >= lb ? 1u : 0u;
+  for (int u = 0; u < E; ++u) n += kv[u] >= lb ? 1u : 0u;
   uint32_t pos = wave_offset<BLOCK>(wave_sum(n), wtot);
   uint32_t total = 0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) total += wtot[i];
-  uint64_t* my = cand + static_cast<size_t>(g) * kChunkCap;
   if (total <= static_cast<uint32_t>(kChunkCap)) {  // else the row falls back: publish the count only
+    const uint32_t e0 = static_cast<uint32_t>(thread_elem0<E>());
 #pragma unroll
     for (int u = 0; u < E; ++u) {
-      const uint32_t key = order_key_bits(raw[u]);
-      const bool hit = key >= lb;
+      const bool hit = kv[u] >= lb;
       const uint64_t m = __ballot(hit);
-      const uint32_t at = pos + lanes_below(m);
-      if (hit) g_store64(&my[at], (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(j0 + u * kWave));
-      pos += static_cast<uint32_t>(__popcll(m));
+      if (m != 0u) {  // most positions of a wavefront have no candidate
+        const uint32_t at = pos + lanes_below(m);
+        if (hit) {
+          hist[at] = kv[u];
+          scol[at] = static_cast<uint16_t>(e0 + u * kWave);
+        }
+        pos += static_cast<uint32_t>(__popcll(m));
+      }
+    }
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        ckeys + static_cast<size_t>(g) * kChunkCap * 4, 0, kChunkCap * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        ccols + static_cast<size_t>(g) * kChunkCap * 2, 0, kChunkCap * 2, 0x00020000);
+    for (uint32_t i = static_cast<uint32_t>(tid); i < total; i += BLOCK) {
+      __builtin_amdgcn_raw_buffer_store_b32(hist[i], krs, i * 4, 0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(scol[i]), crs, i * 2, 0, kCoherent);
     }
   }
   if (tid == 0) {
@@ -1370,9 +1438,46 @@ topk_chunks_kernel(Params p) {
 
   // ---- the row's last workgroup: select among the chunks' candidates ----
   if (tid == 0) g_store(arrived, 0u);  // every workgroup of the row has arrived
+  // Union layout: thread t holds groups q = 0..3 of four consecutive union
+  // entries, group gi = q*BLOCK + t being union entries 4*gi .. 4*gi + 3;
+  // the thread's entry u = 4q + j is union entry 4*gi + j.  Each entry
+  // keeps its candidate slot (chunk << 12 | offset in the chunk's list).
+  // Slotted: chunk c's list fills groups [c*Wg, (c+1)*Wg) with
+  // Wg = 2048 / G (>= 2 since G <= kMaxChunks), so a group's keys are 16
+  // consecutive bytes, loaded at once, before the counts are known; the
+  // quotient by the reciprocal ceil(2^32 / Wg) is exact for gi, Wg < 2^16.
+  // The groups past G*Wg (fewer than G) all read group Wg of the last
+  // chunk, at entries below kChunkCap, which hold zero whenever this union
+  // is used.  The column offsets load behind the radix rounds, which need
+  // them only for ties at the threshold.
+  static_assert(kChunkCap == 4096, "slot = chunk << 12 | offset");
+  static_assert(kUnionPerThread == 16, "four groups of four entries per thread");
+  constexpr int kGroups = kUnionPerThread / 4;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(ckeys, 0, Gr * kChunkCap * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t crs =
+      __builtin_amdgcn_make_buffer_rsrc(ccols, 0, Gr * kChunkCap * 2, 0x00020000);
+  const uint32_t Wg = static_cast<uint32_t>(BLOCK * kGroups / Gr);
+  const uint32_t Wgr = static_cast<uint32_t>((0x100000000ull + Wg - 1) / Wg);
+  uint32_t gslot[kGroups];
+  uint32_t sk[kUnionPerThread];
+#pragma unroll
+  for (int q = 0; q < kGroups; ++q) {
+    const uint32_t gi = static_cast<uint32_t>(q * BLOCK + tid);
+    const uint32_t c = min(__umulhi(gi, Wgr), static_cast<uint32_t>(Gr - 1));
+    gslot[q] = c * static_cast<uint32_t>(kChunkCap) + 4u * min(gi - c * Wg, Wg);
+  }
+#pragma unroll
+  for (int q = 0; q < kGroups; ++q) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(krs, gslot[q] * 4, 0, kCoherent);
+    sk[4 * q + 0] = v.x;
+    sk[4 * q + 1] = v.y;
+    sk[4 * q + 2] = v.z;
+    sk[4 * q + 3] = v.w;
+  }
   if (tid < kWave) {
-    // offsets of the chunks' candidates in the union, total, bounds
-    uint32_t run = 0, lo = 0xFFFFFFFFu, hi = 0u, bad = 0u;
+    // offsets of the chunks' candidates in the packed union, total, bounds
+    uint32_t run = 0, lo = 0xFFFFFFFFu, hi = 0u, bad = 0u, mc = 0u;
     for (int b0 = 0; b0 < Gr; b0 += kWave) {
       const int c = b0 + tid;
       const uint32_t cnt = c < Gr ? g_load(&counts[c]) : 0u;
@@ -1384,108 +1489,140 @@ topk_chunks_kernel(Params p) {
         lo = bnd < lo ? bnd : lo;
         hi = bnd > hi ? bnd : hi;
         bad |= cnt > static_cast<uint32_t>(kChunkCap) ? 1u : 0u;
+        mc = cnt > mc ? cnt : mc;
       }
     }
     hi = wave_max(hi);
     lo = ~wave_max(~lo);
     bad = wave_max(bad);
+    mc = wave_max(mc);
     if (tid == 0) {
       coff[Gr] = run;
       res[5] = run;
       res[6] = lo;
       res[7] = hi;
       res[8] = bad;
+      res[10] = mc;
       res[3] = 0u;
     }
   }
   __syncthreads();
   const uint32_t utotal = res[5], min_lb = res[6], max_lb = res[7];
-  const bool exact_ok = res[8] == 0u && utotal >= kk &&
-                  utotal <= static_cast<uint32_t>(BLOCK * kUnionPerThread);
+  const bool fits = res[8] == 0u && utotal >= kk;
+  const bool slotted = fits && res[10] <= 4u * Wg;
+  const bool exact_ok =
+      fits && (slotted || utotal <= static_cast<uint32_t>(BLOCK * kUnionPerThread));
   bool done = false;
   if (exact_ok) {
-    // union entry i = s*BLOCK + t goes to thread t, slot s (consecutive
-    // threads read consecutive candidates).  A map from union entry to chunk
-    // (16-bit, in the histogram's LDS; wavefront w fills the chunks
-    // c = w mod NW) lets all of a thread's loads issue back to back.
-    uint16_t* chunk_of = reinterpret_cast<uint16_t*>(hist);
-    for (int c = static_cast<int>(wave_id()); c < Gr; c += NW)
-      for (uint32_t i = coff[c] + __lane_id(); i < coff[c + 1]; i += kWave)
-        chunk_of[i] = static_cast<uint16_t>(c);
-    __syncthreads();
-    UnionList un;
-    {
-      const uint32_t t = static_cast<uint32_t>(tid);
-      uint32_t at[kUnionPerThread];
-      uint64_t e[kUnionPerThread];
+    UnionList<BLOCK * E> un;
+    if (slotted) {
 #pragma unroll
-      for (int sl = 0; sl < kUnionPerThread; ++sl) {
-        const uint32_t i = static_cast<uint32_t>(sl * BLOCK) + t;
+      for (int u = 0; u < kUnionPerThread; ++u) un.sat[u] = gslot[u / 4] + static_cast<uint32_t>(u % 4);
+    } else {
+      // packed union: the same entry order over the chunks' lists laid end
+      // to end; a map from union entry to chunk (16-bit, in the histogram's
+      // LDS; wavefront w fills the chunks c = w mod NW) gives each slot
+      uint16_t* chunk_of = reinterpret_cast<uint16_t*>(hist);
+      for (int c = static_cast<int>(wave_id()); c < Gr; c += NW)
+        for (uint32_t i = coff[c] + __lane_id(); i < coff[c + 1]; i += kWave)
+          chunk_of[i] = static_cast<uint16_t>(c);
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kUnionPerThread; ++u) {
+        const uint32_t i = 4u * static_cast<uint32_t>((u / 4) * BLOCK + tid) + static_cast<uint32_t>(u % 4);
         const bool ok = i < utotal;
         const uint32_t c = ok ? chunk_of[i] : 0u;
-        at[sl] = ok ? c * static_cast<uint32_t>(kChunkCap) + (i - coff[c]) : 0u;
+        un.sat[u] = ok ? c * static_cast<uint32_t>(kChunkCap) + (i - coff[c]) : 0xFFFFFFFFu;
       }
 #pragma unroll
-      for (int sl = 0; sl < kUnionPerThread; ++sl) e[sl] = g_load64(&cand[at[sl]]);
-      uint32_t mx = 0;
-#pragma unroll
-      for (int sl = 0; sl < kUnionPerThread; ++sl) {
-        const bool ok = static_cast<uint32_t>(sl * BLOCK) + t < utotal;
-        un.key[sl] = ok ? static_cast<uint32_t>(e[sl] >> 32) : 0u;
-        un.col[sl] = static_cast<int32_t>(static_cast<uint32_t>(e[sl]));
-        mx = max(mx, un.key[sl]);
-      }
-      // the candidates are in registers: return their slots to zero (other
-      // paths may use the workspace next)
-#pragma unroll
-      for (int sl = 0; sl < kUnionPerThread; ++sl)
-        if (un.key[sl] != 0u) g_store64(&cand[at[sl]], 0ull);
-      mx = wave_max(mx);
-      if (__lane_id() == 0) atomicMax(&res[3], mx);
+      for (int u = 0; u < kUnionPerThread; ++u)
+        sk[u] = un.sat[u] != 0xFFFFFFFFu
+                    ? __builtin_amdgcn_raw_buffer_load_b32(krs, un.sat[u] * 4, 0, kCoherent)
+                    : 0u;
+      __syncthreads();  // chunk_of (the histogram's words) is reused
     }
+    uint32_t mx = 0;
+#pragma unroll
+    for (int u = 0; u < kUnionPerThread; ++u) {
+      un.key[u] = sk[u];
+      mx = max(mx, sk[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnionPerThread; ++u)
+      un.off[u] = __builtin_amdgcn_raw_buffer_load_b16(crs, (un.key[u] != 0u ? un.sat[u] : 0u) * 2, 0, kCoherent);
+    mx = wave_max(mx);
+    if (__lane_id() == 0) atomicMax(&res[3], mx);
     __syncthreads();
     const uint32_t kmax = res[3];
     const Prefix pf = rounds_window<BLOCK>(un, min_lb, kmax, kk, ib, hist, res);
     // every selected key is at least the selected bucket's lower edge
     const uint32_t edge = pf.bits >= 32 ? pf.kp : (pf.kp << (32 - pf.bits));
     if (edge >= max_lb) {
-      // ordered emission: the union's order is (slot, thread); per slot and
-      // wavefront counts give each selected entry its rank
-      uint32_t* wslot = hist;                            // [slot][wave] counts
-      uint32_t* pre = hist + kUnionPerThread * NW;       // [slot][wave] offsets
+      // ordered emission.  The union's order is (group q, wavefront, lane,
+      // j), so a selected entry's rank is: the selected entries of the
+      // (q, wavefront) pairs before its own (an exclusive prefix over the
+      // 4*NW pair totals, which every wavefront takes itself), plus those
+      // of the lanes below in its wavefront's group q, plus those of its
+      // own group before j.  The columns go to LDS at their ranks, then out
+      // in order.
+      uint32_t* stage = hist;  // k <= kChunkCap columns
       const uint32_t w = wave_id();
+      const uint32_t lane = __lane_id();
       with_pred(pf, ib, rmask, [&](const auto& pred) {
-        uint64_t m[kUnionPerThread];
+        uint32_t sel = 0;
 #pragma unroll
-        for (int sl = 0; sl < kUnionPerThread; ++sl) {
-          m[sl] = __ballot(pred.ge(un.key[sl], un.col[sl]));
-          if (__lane_id() == 0) wslot[sl * NW + w] = static_cast<uint32_t>(__popcll(m[sl]));
+        for (int u = 0; u < kUnionPerThread; ++u)
+          sel |= pred.ge(un.key[u], un.col(u)) ? (1u << u) : 0u;
+        uint32_t below[kGroups];
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) {
+          const uint32_t c = static_cast<uint32_t>(__builtin_popcount((sel >> (4 * q)) & 15u));
+          const uint32_t incl = wave_inclusive_sum(c);
+          below[q] = incl - c;
+          if (lane == kWave - 1) wq[q * NW + w] = incl;
         }
         __syncthreads();
-        if (tid < kWave) {
-          // lane l < kUnionPerThread: slot l's total; a prefix over the lanes
-          // gives each slot's start, then every (slot, wavefront) pair its
-          // offset
-          uint32_t tot = 0;
-          if (tid < kUnionPerThread)
-            for (int i = 0; i < NW; ++i) tot += wslot[tid * NW + i];
-          const uint32_t start = wave_inclusive_sum(tot) - tot;
-          for (int q = tid; q < kUnionPerThread * NW; q += kWave) {
-            const int sl = q / NW, wv = q % NW;
-            uint32_t before = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(sl << 2, static_cast<int>(start)));
-            for (int i = 0; i < wv; ++i) before += wslot[sl * NW + i];
-            pre[q] = before;
+        const uint32_t v = lane < static_cast<uint32_t>(kGroups * NW) ? wq[lane] : 0u;
+        const uint32_t ex = wave_inclusive_sum(v) - v;
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) {
+          uint32_t r = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ex), q * NW + static_cast<int>(w))) +
+                       below[q];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int u = 4 * q + j;
+            if ((sel >> u) & 1u) {
+              if (r < kk) stage[r] = static_cast<uint32_t>(un.col(u));
+              ++r;
+            }
           }
         }
         __syncthreads();
-#pragma unroll
-        for (int sl = 0; sl < kUnionPerThread; ++sl) {
-          const uint32_t at = pre[sl * NW + w] + lanes_below(m[sl]);
-          if (((m[sl] >> __lane_id()) & 1u) && at < kk) out_row[at] = un.col[sl];
+        if ((reinterpret_cast<uintptr_t>(out_row) & 15u) == 0 && (kk & 3u) == 0) {
+          for (uint32_t i = 4u * static_cast<uint32_t>(tid); i < kk; i += 4u * BLOCK)
+            *reinterpret_cast<uint4*>(out_row + i) = *reinterpret_cast<const uint4*>(stage + i);
+        } else {
+          for (uint32_t i = static_cast<uint32_t>(tid); i < kk; i += BLOCK)
+            out_row[i] = static_cast<int32_t>(stage[i]);
         }
       });
     }
     done = edge >= max_lb;
+    // the slots read return to zero (other paths may use the workspace next)
+    if (slotted) {
+#pragma unroll
+      for (int q = 0; q < kGroups; ++q) {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, krs, gslot[q] * 4, 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, crs, gslot[q] * 2, 0, kCoherent);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kUnionPerThread; ++u)
+        if (un.key[u] != 0u) {
+          __builtin_amdgcn_raw_buffer_store_b32(0u, krs, un.sat[u] * 4, 0, kCoherent);
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(0), crs, un.sat[u] * 2, 0, kCoherent);
+        }
+    }
     __syncthreads();
   }
   if (!done) select_row_streamed<BLOCK>(row_ptr, L, p.k, out_row, hist, wtot, res);
@@ -1493,8 +1630,11 @@ topk_chunks_kernel(Params p) {
     for (int c = 0; c < Gr; ++c) {
       const uint32_t cnt = coff[c + 1] - coff[c];
       const uint32_t used = cnt <= static_cast<uint32_t>(kChunkCap) ? cnt : 0u;  // see the publish
-      for (uint32_t j = static_cast<uint32_t>(tid); j < used; j += BLOCK)
-        g_store64(&cand[static_cast<size_t>(c) * kChunkCap + j], 0ull);
+      for (uint32_t j = static_cast<uint32_t>(tid); j < used; j += BLOCK) {
+        const uint32_t at = static_cast<uint32_t>(c) * kChunkCap + j;
+        __builtin_amdgcn_raw_buffer_store_b32(0u, krs, at * 4, 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(0), crs, at * 2, 0, kCoherent);
+      }
     }
   }
   for (int c = tid; c < Gr; c += BLOCK) {
