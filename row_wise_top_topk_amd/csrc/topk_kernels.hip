@@ -1173,10 +1173,12 @@ __host__ __device__ constexpr size_t chunk_row_bytes(int G) {
 template <int CHUNK>
 struct UnionList {
   uint32_t key[kUnionPerThread];
-  uint32_t sat[kUnionPerThread];  // candidate slot: chunk << 12 | offset in the chunk's list
-  uint32_t off[kUnionPerThread];  // column offset within the chunk (loaded late)
+  uint32_t sat[kUnionPerThread];      // candidate slot: chunk << 12 | offset in the chunk's list
+  u32x2 offw[kUnionPerThread / 4];    // column offsets within the chunk, 16 bits each (loaded late)
   __device__ __forceinline__ int32_t col(int u) const {
-    return static_cast<int32_t>((sat[u] >> 12) * static_cast<uint32_t>(CHUNK) + off[u]);
+    const uint32_t w2 = (u & 2) ? offw[u >> 2].y : offw[u >> 2].x;
+    const uint32_t off = (u & 1) ? (w2 >> 16) : (w2 & 0xFFFFu);
+    return static_cast<int32_t>((sat[u] >> 12) * static_cast<uint32_t>(CHUNK) + off);
   }
   template <class F>
   __device__ __forceinline__ void operator()(F f) const {
@@ -1547,11 +1549,24 @@ topk_chunks_kernel(Params p) {
       un.key[u] = sk[u];
       mx = max(mx, sk[u]);
     }
-#pragma unroll
-    for (int u = 0; u < kUnionPerThread; ++u)
-      un.off[u] = __builtin_amdgcn_raw_buffer_load_b16(crs, (un.key[u] != 0u ? un.sat[u] : 0u) * 2, 0, kCoherent);
     mx = wave_max(mx);
     if (__lane_id() == 0) atomicMax(&res[3], mx);
+    // the keys are consumed before the column loads go out, so no wait
+    // for those loads comes before the emission needs them
+    asm volatile("" ::: "memory");
+    if (slotted) {
+#pragma unroll
+      for (int q = 0; q < kGroups; ++q)
+        un.offw[q] = __builtin_amdgcn_raw_buffer_load_b64(crs, gslot[q] * 2, 0, kCoherent);
+    } else {
+      uint32_t o[kUnionPerThread];
+#pragma unroll
+      for (int u = 0; u < kUnionPerThread; ++u)
+        o[u] = un.key[u] != 0u ? __builtin_amdgcn_raw_buffer_load_b16(crs, un.sat[u] * 2, 0, kCoherent) : 0u;
+#pragma unroll
+      for (int q = 0; q < kGroups; ++q)
+        un.offw[q] = u32x2{o[4 * q] | (o[4 * q + 1] << 16), o[4 * q + 2] | (o[4 * q + 3] << 16)};
+    }
     __syncthreads();
     const uint32_t kmax = res[3];
     const Prefix pf = rounds_window<BLOCK>(un, min_lb, kmax, kk, ib, hist, res);

@@ -174,6 +174,27 @@ def test_paths_share_one_workspace():
             assert int(ws.count_nonzero()) == 0, path
 
 
+def test_chunks_long_workload_leaves_workspace_zero():
+    # the small-batch long-context shape (55 chunks per row: the final
+    # workgroup reads the chunks' keys in whole 16-byte groups), then tied
+    # levels on the same shape (chunks overflow their groups or the union):
+    # repeated calls on one workspace, each exact and each leaving it zero
+    base = workloads.make("long")
+    lengths = base.lengths.tolist()
+    wls = [base, workloads.make_custom(base.num_rows, base.row_stride, lengths, base.k,
+                                       seed=43, kind="levels")]
+    need = mt.workspace_size(base.num_rows, base.row_stride, base.k, path="chunks")
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    for wl in wls:
+        logits, lens = device_view(wl)
+        ref = expected(wl)
+        for _ in range(3):
+            out = mt.topk_indices(logits, lens, wl.k, workspace=ws, path="chunks")
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), ref)
+            assert int(ws.count_nonzero()) == 0
+
+
 def test_chunks_cluster_in_one_chunk():
     # one chunk holds a block of 3000 equal high values: its count exceeds the
     # last workgroup's fixed window, so the union is gathered through the
