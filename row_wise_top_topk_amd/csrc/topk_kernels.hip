@@ -1154,7 +1154,7 @@ topk_split_kernel(Params p) {
 // ---------------------------------------------------------------------------
 constexpr int kChunkCap = 4096;       // candidates one chunk may publish
 constexpr int kUnionPerThread = 16;   // candidates per thread in the final selection
-constexpr int kChunkSamples = 16;     // sample positions per thread
+constexpr int kChunkSamples = 16;     // sample positions per thread (the first half)
 
 // Row r's block in the workspace (after the header) starts at
 // r * chunk_row_bytes(G): a 256-byte head whose word 0 counts the row's
@@ -1331,12 +1331,36 @@ topk_chunks_kernel(Params p) {
     select_chunk_whole_row<BLOCK, E>(raw1, ch, L, p.k, out_row, hist, wtot, res);
     return;
   }
+  // The chunk's raw bits, every load issued at once (past the row they read
+  // nothing).  They become keys in place; positions past the row get key 1,
+  // below every bound and skipped by the sample.  The sample is the thread's
+  // first kChunkSamples positions (the first half of each wavefront's
+  // stretch of the chunk), so it is taken while the second half is still
+  // arriving; that half becomes keys after the bound.  (No branch touches a
+  // loaded word before its conversion: a register copy where two paths
+  // join would make the wave wait for every load issued before it.)
+  static_assert(2 * kChunkSamples == E, "the sample is the first half");
   uint32_t kv[E];
-  load_raw<BLOCK, E>(kv, ch);
-  // keys in place; positions outside the row (kOutsideBits) get key 1, below
-  // every bound and skipped by the sample
+  const int e0 = thread_elem0<E>();
+  {
+    const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(ch.base), 0, clen * 4, 0x00020000);
 #pragma unroll
-  for (int u = 0; u < E; ++u) kv[u] = order_key_bits(kv[u]);
+    for (int u = 0; u < E; ++u)
+      kv[u] = __builtin_amdgcn_raw_buffer_load_b32(rrs, (e0 + u * kWave) * 4, 0, 0);
+  }
+  const bool whole = clen == chunk;
+  auto to_keys = [&](auto first, auto last) {
+    if (whole) {
+#pragma unroll
+      for (int u = decltype(first)::value; u < decltype(last)::value; ++u) kv[u] = order_key_bits(kv[u]);
+    } else {
+#pragma unroll
+      for (int u = decltype(first)::value; u < decltype(last)::value; ++u)
+        kv[u] = e0 + u * kWave < clen ? order_key_bits(kv[u]) : 1u;
+    }
+  };
+  to_keys(std::integral_constant<int, 0>{}, std::integral_constant<int, kChunkSamples>{});
 
   uint8_t* rb = p.ws + kWsHeader + static_cast<size_t>(row) * chunk_row_bytes(G);
   uint32_t* arrived = reinterpret_cast<uint32_t*>(rb);
@@ -1345,13 +1369,13 @@ topk_chunks_kernel(Params p) {
   uint8_t* ckeys = rb + 256 + ((8 * static_cast<size_t>(G) + 255) / 256) * 256;  // u32 [G][kChunkCap]
   uint8_t* ccols = ckeys + static_cast<size_t>(G) * kChunkCap * 4;                 // u16 [G][kChunkCap]
 
-  // sample: kChunkSamples positions per thread, spread over its E positions
+  // sample: the first kChunkSamples positions of each thread
   for (int i = tid; i < kFirstBins; i += BLOCK) hist[i] = 0;
   if (tid == 0) res[0] = 0u;
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < kChunkSamples; ++q) {
-    const uint32_t key = kv[q * (E / kChunkSamples)];
+    const uint32_t key = kv[q];
     hist_add_wave(hist, key >> (32 - kFirstBits), key > 1u);  // kOutsideBits: key 1
   }
   __syncthreads();
@@ -1379,7 +1403,7 @@ topk_chunks_kernel(Params p) {
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < kChunkSamples; ++q) {
-      const uint32_t key = kv[q * (E / kChunkSamples)];
+      const uint32_t key = kv[q];
       hist_add_wave(hist, (key >> (32 - kFirstBits - kNextBits)) & (kNextBins - 1),
                     (key >> (32 - kFirstBits)) == b0);
     }
@@ -1388,6 +1412,8 @@ topk_chunks_kernel(Params p) {
     __syncthreads();
     lb = (b0 << (32 - kFirstBits)) | (res[0] << (32 - kFirstBits - kNextBits));
   }
+
+  to_keys(std::integral_constant<int, kChunkSamples>{}, std::integral_constant<int, E>{});
 
   // publish the chunk's entries with key >= lb, in column order: staged in
   // LDS (keys in the histogram's words, column offsets in scol), then
@@ -1400,7 +1426,6 @@ topk_chunks_kernel(Params p) {
 #pragma unroll
   for (int i = 0; i < NW; ++i) total += wtot[i];
   if (total <= static_cast<uint32_t>(kChunkCap)) {  // else the row falls back: publish the count only
-    const uint32_t e0 = static_cast<uint32_t>(thread_elem0<E>());
 #pragma unroll
     for (int u = 0; u < E; ++u) {
       const bool hit = kv[u] >= lb;
