@@ -302,6 +302,71 @@ __device__ __forceinline__ uint32_t find_bucket_wave_nb(const uint32_t* hist, Ne
   return total;
 }
 
+// The same search with every thread of the workgroup and one barrier:
+// thread t sums group t of GS = NB/BLOCK adjacent bins counted from the top
+// (one bin, for t < NB, when NB < BLOCK; read with 16-byte LDS loads when GS
+// is a multiple of 4), a wavefront prefix sum and the wavefronts' totals (in
+// wt[0..NW)) give each group the count above it, and the thread whose group
+// crosses `need` walks its bins.  need_of(total) gives `need` from the
+// histogram's total.  Result in res[0..2]; nothing is written when need is 0
+// or above the total.  Every thread must call it; the caller synchronises
+// before reading res (and before reusing wt).
+template <int BLOCK, int NB, class NeedOf>
+__device__ __forceinline__ void find_bucket_block(const uint32_t* hist, NeedOf need_of, uint32_t* res,
+                                                  uint32_t* wt) {
+  static_assert(NB >= 2 && (NB & (NB - 1)) == 0, "power-of-two bin count");
+  constexpr int NW = BLOCK / kWave;
+  constexpr int GS = NB >= BLOCK ? NB / BLOCK : 1;
+  const int t = static_cast<int>(threadIdx.x);
+  const bool live = t * GS < NB;
+  const int top = NB - t * GS;  // this thread's bins: [top - GS, top)
+  uint32_t h[GS];               // h[i]: bin top - 1 - i
+  if constexpr (GS % 4 == 0) {
+#pragma unroll
+    for (int v = 0; v < GS / 4; ++v) {
+      const uint4 q = *reinterpret_cast<const uint4*>(hist + top - 4 * (v + 1));
+      h[4 * v + 0] = q.w;
+      h[4 * v + 1] = q.z;
+      h[4 * v + 2] = q.y;
+      h[4 * v + 3] = q.x;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < GS; ++i) h[i] = live ? hist[top - 1 - i] : 0u;
+  }
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < GS; ++i) s += h[i];
+  const uint32_t incl = wave_inclusive_sum(s);
+  const int w = t / kWave;
+  if ((t & (kWave - 1)) == kWave - 1) wt[w] = incl;
+  __syncthreads();
+  uint32_t above = 0, total = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const uint32_t x = wt[v];
+    above += v < w ? x : 0u;
+    total += x;
+  }
+  const uint32_t need = need_of(total);
+  if (need == 0u || need > total) return;
+  const uint32_t a = above + incl - s;  // entries in the groups above this one
+  if (live && a < need && a + s >= need) {
+    uint32_t run = a;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < GS; ++i) {
+      if (!found && run + h[i] >= need) {
+        res[0] = static_cast<uint32_t>(top - 1 - i);
+        res[1] = run;
+        res[2] = h[i];
+        found = true;
+      }
+      run += h[i];
+    }
+  }
+}
+
 // find_bucket_wave_nb for a bin count known only at run time (a power of two
 // from 2 to 4096).
 __device__ __forceinline__ void find_bucket_wave(const uint32_t* hist, int nb, uint32_t need,
@@ -332,7 +397,8 @@ __device__ __forceinline__ void find_bucket_wave(const uint32_t* hist, int nb, u
   }
 }
 
-// Radix rounds inside one workgroup.  `src.count(p, d, ib, rmask, hist)`
+// Radix rounds inside one workgroup (wt: NW words of LDS scratch).
+// `src.count(p, d, ib, rmask, hist)`
 // histograms digit d below prefix p (p.bits == 0: all entries).  Starting
 // from prefix p with `need` entries still to choose among p's bucket, the
 // prefix is refined one digit at a time until the bucket holding the need-th
@@ -340,7 +406,7 @@ __device__ __forceinline__ void find_bucket_wave(const uint32_t* hist, int nb, u
 // selected entries are those whose composite prefix is >= it.
 template <int BLOCK, class Src>
 __device__ __forceinline__ Prefix rounds_local(const Src& src, Prefix p, uint32_t need, int ib,
-                                               uint32_t* hist, uint32_t* res) {
+                                               uint32_t* hist, uint32_t* res, uint32_t* wt) {
   const uint32_t rmask = (1u << ib) - 1u;
   for (int round = 0; round < kMaxRounds + 1; ++round) {
     const int d = digit_bits(p.bits, ib);
@@ -371,7 +437,7 @@ __device__ __forceinline__ Prefix rounds_local(const Src& src, Prefix p, uint32_
 template <int BLOCK, class Src>
 __device__ __forceinline__ Prefix rounds_window(const Src& src, uint32_t lo, uint32_t hi,
                                                 uint32_t need, int ib, uint32_t* hist,
-                                                uint32_t* res) {
+                                                uint32_t* res, uint32_t* wt) {
   int s = 0;
   while ((hi >> s) - (lo >> s) >= static_cast<uint32_t>(kFirstBins)) ++s;
   const uint32_t base = lo >> s;
@@ -381,13 +447,13 @@ __device__ __forceinline__ Prefix rounds_window(const Src& src, uint32_t lo, uin
     if (key != 0u) atomicAdd(&hist[(key >> s) - base], 1u);
   });
   __syncthreads();
-  if (threadIdx.x < kWave) find_bucket_wave_nb<kFirstBins>(hist, [need](uint32_t) { return need; }, res);
+  find_bucket_block<BLOCK, kFirstBins>(hist, [need](uint32_t) { return need; }, res, wt);
   __syncthreads();
   const uint32_t b = res[0], gt = res[1], cnt = res[2];
   need -= gt;
   const Prefix p{32 - s, base + b, 0u};
   if (cnt == need) return p;
-  return rounds_local<BLOCK>(src, p, need, ib, hist, res);
+  return rounds_local<BLOCK>(src, p, need, ib, hist, res, wt);
 }
 
 }  // namespace mitopk

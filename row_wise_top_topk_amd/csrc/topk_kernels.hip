@@ -502,7 +502,7 @@ __device__ __forceinline__ void select_row(uint32_t (&raw)[E], const Chunk& ch, 
         lst.key[u] = ok ? order_key_bits(lds.lraw[a]) : 0u;
         lst.col[u] = ok ? static_cast<int32_t>(lds.lcol[a]) : 0;
       }
-      const Prefix pf = rounds_local<BLOCK>(lst, Prefix{0, 0u, 0u}, kk, ib, lds.hist, lds.res);
+      const Prefix pf = rounds_local<BLOCK>(lst, Prefix{0, 0u, 0u}, kk, ib, lds.hist, lds.res, lds.wtot);
       with_pred(pf, ib, rmask, [&](const auto& pred) {
         uint32_t n = 0;
 #pragma unroll
@@ -529,7 +529,7 @@ __device__ __forceinline__ void select_row(uint32_t (&raw)[E], const Chunk& ch, 
     if (sampled) load_raw<BLOCK, E>(raw, ch);
     keys_in_place<BLOCK, E>(raw, ch);
     const Prefix pf =
-        rounds_local<BLOCK>(RegSource<BLOCK, E>{raw, ch}, Prefix{0, 0u, 0u}, kk, ib, lds.hist, lds.res);
+        rounds_local<BLOCK>(RegSource<BLOCK, E>{raw, ch}, Prefix{0, 0u, 0u}, kk, ib, lds.hist, lds.res, lds.wtot);
     emit_ordered<BLOCK, E>(raw, ch, pf, ib, out_row, 0u, kk, lds.wtot);
   }
 }
@@ -683,7 +683,7 @@ __device__ __forceinline__ void select_stream_exact(const StreamGeom<BLOCK, NP>&
   const int ib = index_bits(L);
   const uint32_t rmask = (1u << ib) - 1u;
   const uint32_t kk = static_cast<uint32_t>(k);
-  const Prefix pf = rounds_local<BLOCK>(g, Prefix{0, 0u, 0u}, kk, ib, lds.u.hist, lds.res);
+  const Prefix pf = rounds_local<BLOCK>(g, Prefix{0, 0u, 0u}, kk, ib, lds.u.hist, lds.res, lds.wtot);
   with_pred(pf, ib, rmask, [&](const auto& pred) {
     uint32_t n = 0;
     g([&](uint32_t key, int32_t j) { n += pred.ge(key, j) ? 1u : 0u; });
@@ -792,7 +792,7 @@ topk_stream_kernel(Params p) {
     load_raw<BLOCK, kChunkPos>(key, ch);
     keys_in_place<BLOCK, kChunkPos>(key, ch);
     const Prefix pf = rounds_local<BLOCK>(RegSource<BLOCK, kChunkPos>{key, ch}, Prefix{0, 0u, 0u},
-                                          kk, ib, lds.u.hist, lds.res);
+                                          kk, ib, lds.u.hist, lds.res, lds.wtot);
     emit_ordered<BLOCK, kChunkPos>(key, ch, pf, ib, out_row, 0u, kk, lds.wtot);
     return;
   }
@@ -829,15 +829,13 @@ topk_stream_kernel(Params p) {
     }
   }
   __syncthreads();
-  if (tid < kWave) {
-    if (tid == 0) lds.res[0] = 0u;
-    find_bucket_wave_nb<kFirstBins>(
-        lds.u.hist,
-        [&](uint32_t ns) {
-          return static_cast<uint32_t>((5ull * kk * ns + 4ull * L - 1) / (4ull * L)) + 8u;
-        },
-        lds.res);
-  }
+  if (tid == 0) lds.res[0] = 0u;
+  find_bucket_block<BLOCK, kFirstBins>(
+      lds.u.hist,
+      [&](uint32_t ns) {
+        return static_cast<uint32_t>((5ull * kk * ns + 4ull * L - 1) / (4ull * L)) + 8u;
+      },
+      lds.res, lds.wtot);
   __syncthreads();
   uint32_t lb = lds.res[0] << (32 - kFirstBits);
   lb = lb < 2u ? 2u : lb;
@@ -895,7 +893,7 @@ topk_stream_kernel(Params p) {
   __syncthreads();  // the list's LDS becomes the histogram
   // every listed key lies in [lb, largest]
   const uint32_t kmax = lds.res[3];
-  const Prefix pf = rounds_window<BLOCK>(lst, lb, kmax, kk, ib, lds.u.hist, lds.res);
+  const Prefix pf = rounds_window<BLOCK>(lst, lb, kmax, kk, ib, lds.u.hist, lds.res, lds.wtot);
   with_pred(pf, ib, rmask, [&](const auto& pred) {
     uint32_t n = 0;
 #pragma unroll
@@ -940,7 +938,7 @@ __device__ __forceinline__ void select_chunk_whole_row(const uint32_t (&key)[E],
   const int ib = index_bits(L);
   const uint32_t kk = static_cast<uint32_t>(k);
   const Prefix pf =
-      rounds_local<BLOCK>(RegSource<BLOCK, E>{key, ch}, Prefix{0, 0u, 0u}, kk, ib, hist, res);
+      rounds_local<BLOCK>(RegSource<BLOCK, E>{key, ch}, Prefix{0, 0u, 0u}, kk, ib, hist, res, wtot);
   emit_ordered<BLOCK, E>(key, ch, pf, ib, out_row, 0u, kk, wtot);
 }
 
@@ -1075,7 +1073,7 @@ topk_split_kernel(Params p) {
       const int nc = static_cast<int>(cnt);
       for (int i = tid; i < nc; i += BLOCK) cand[i] = g_load64(&ws->cand[i]);
       __syncthreads();
-      pf = rounds_local<BLOCK>(ListSource<BLOCK>{cand, nc}, pr, need, ib, hist, res);
+      pf = rounds_local<BLOCK>(ListSource<BLOCK>{cand, nc}, pr, need, ib, hist, res, wtot);
       for (int i = tid; i < Gr; i += BLOCK) csel[i] = 0;
       __syncthreads();
       with_pred(pf, ib, rmask, [&](const auto& pred) {
@@ -1266,7 +1264,7 @@ __device__ __forceinline__ void select_row_streamed(const float* row, int L, int
   const int ib = index_bits(L);
   const uint32_t rmask = (1u << ib) - 1u;
   const uint32_t kk = static_cast<uint32_t>(k);
-  const Prefix pf = rounds_local<BLOCK>(src, Prefix{0, 0u, 0u}, kk, ib, hist, res);
+  const Prefix pf = rounds_local<BLOCK>(src, Prefix{0, 0u, 0u}, kk, ib, hist, res, wtot);
   with_pred(pf, ib, rmask, [&](const auto& pred) {
     uint32_t out_base = 0;
     src.blocks([&](const uint32_t (&buf)[kChunkPos], int e0) {
@@ -1379,16 +1377,14 @@ topk_chunks_kernel(Params p) {
     hist_add_wave(hist, key >> (32 - kFirstBits), key > 1u);  // kOutsideBits: key 1
   }
   __syncthreads();
-  if (tid < kWave) {
-    find_bucket_wave_nb<kFirstBins>(
-        hist,
-        [&](uint32_t ns) {
-          const uint32_t nd = static_cast<uint32_t>((3ull * kk * ns + 2ull * L - 1) / (2ull * L)) + 16u;
-          if (__lane_id() == 0) res[9] = nd;
-          return nd;
-        },
-        res);
-  }
+  find_bucket_block<BLOCK, kFirstBins>(
+      hist,
+      [&](uint32_t ns) {
+        const uint32_t nd = static_cast<uint32_t>((3ull * kk * ns + 2ull * L - 1) / (2ull * L)) + 16u;
+        if (tid == 0) res[9] = nd;
+        return nd;
+      },
+      res, wtot);
   __syncthreads();
   // The first-digit bin holding the need-th sample is refined by the next
   // digit, so the bound sits at that sample (to 22 bits) rather than at the
@@ -1408,7 +1404,7 @@ topk_chunks_kernel(Params p) {
                     (key >> (32 - kFirstBits)) == b0);
     }
     __syncthreads();
-    if (tid < kWave) find_bucket_wave_nb<kNextBins>(hist, [need2](uint32_t) { return need2; }, res);
+    find_bucket_block<BLOCK, kNextBins>(hist, [need2](uint32_t) { return need2; }, res, wtot);
     __syncthreads();
     lb = (b0 << (32 - kFirstBits)) | (res[0] << (32 - kFirstBits - kNextBits));
   }
@@ -1594,7 +1590,7 @@ topk_chunks_kernel(Params p) {
     }
     __syncthreads();
     const uint32_t kmax = res[3];
-    const Prefix pf = rounds_window<BLOCK>(un, min_lb, kmax, kk, ib, hist, res);
+    const Prefix pf = rounds_window<BLOCK>(un, min_lb, kmax, kk, ib, hist, res, wtot);
     // every selected key is at least the selected bucket's lower edge
     const uint32_t edge = pf.bits >= 32 ? pf.kp : (pf.kp << (32 - pf.bits));
     if (edge >= max_lb) {
