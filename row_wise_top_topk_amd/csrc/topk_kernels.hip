@@ -1411,38 +1411,80 @@ topk_chunks_kernel(Params p) {
 
   to_keys(std::integral_constant<int, kChunkSamples>{}, std::integral_constant<int, E>{});
 
-  // publish the chunk's entries with key >= lb, in column order: staged in
-  // LDS (keys in the histogram's words, column offsets in scol), then
-  // written out by consecutive threads
-  uint32_t n = 0;
+  // Publish the chunk's entries with key >= lb, in column order.  Each
+  // wavefront stages its candidates in its own region of kWaveStage LDS
+  // entries (keys in the histogram's words, column offsets in scol) while
+  // counting them; the wavefronts' counts then place the regions one after
+  // another, and consecutive threads write the list out.  A wavefront with
+  // more candidates than its region sends the chunk through the same steps
+  // with positions counted first (one region for the whole chunk).
+  constexpr uint32_t kWaveStage = kChunkCap / NW;
+  const uint32_t wv = wave_id();
+  uint32_t pos = 0;  // this wavefront's candidates so far (uniform)
 #pragma unroll
-  for (int u = 0; u < E; ++u) n += kv[u] >= lb ? 1u : 0u;
-  uint32_t pos = wave_offset<BLOCK>(wave_sum(n), wtot);
-  uint32_t total = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) total += wtot[i];
-  if (total <= static_cast<uint32_t>(kChunkCap)) {  // else the row falls back: publish the count only
-#pragma unroll
-    for (int u = 0; u < E; ++u) {
-      const bool hit = kv[u] >= lb;
-      const uint64_t m = __ballot(hit);
-      if (m != 0u) {  // most positions of a wavefront have no candidate
-        const uint32_t at = pos + lanes_below(m);
-        if (hit) {
-          hist[at] = kv[u];
-          scol[at] = static_cast<uint16_t>(e0 + u * kWave);
-        }
-        pos += static_cast<uint32_t>(__popcll(m));
+  for (int u = 0; u < E; ++u) {
+    const bool hit = kv[u] >= lb;
+    const uint64_t m = __ballot(hit);
+    if (m != 0u) {  // most positions of a wavefront have no candidate
+      const uint32_t at = pos + lanes_below(m);
+      if (hit && at < kWaveStage) {
+        hist[wv * kWaveStage + at] = kv[u];
+        scol[wv * kWaveStage + at] = static_cast<uint16_t>(e0 + u * kWave);
       }
+      pos += static_cast<uint32_t>(__popcll(m));
     }
-    __syncthreads();
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        ckeys + static_cast<size_t>(g) * kChunkCap * 4, 0, kChunkCap * 4, 0x00020000);
-    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-        ccols + static_cast<size_t>(g) * kChunkCap * 2, 0, kChunkCap * 2, 0x00020000);
-    for (uint32_t i = static_cast<uint32_t>(tid); i < total; i += BLOCK) {
-      __builtin_amdgcn_raw_buffer_store_b32(hist[i], krs, i * 4, 0, kCoherent);
-      __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(scol[i]), crs, i * 2, 0, kCoherent);
+  }
+  if (__lane_id() == 0) wtot[wv] = pos;
+  __syncthreads();
+  uint32_t woff[NW + 1];
+  woff[0] = 0;
+  bool spill = false;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const uint32_t c = wtot[v];
+    woff[v + 1] = woff[v] + c;
+    spill |= c > kWaveStage;
+  }
+  const uint32_t total = woff[NW];
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+      ckeys + static_cast<size_t>(g) * kChunkCap * 4, 0, kChunkCap * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t pcs = __builtin_amdgcn_make_buffer_rsrc(
+      ccols + static_cast<size_t>(g) * kChunkCap * 2, 0, kChunkCap * 2, 0x00020000);
+  if (total <= static_cast<uint32_t>(kChunkCap)) {  // else the row falls back: publish the count only
+    if (!spill) {
+      for (uint32_t i = static_cast<uint32_t>(tid); i < total; i += BLOCK) {
+        uint32_t v = 0, base = 0;  // the region holding list entry i
+#pragma unroll
+        for (int x = 1; x < NW; ++x) {
+          const bool in = i >= woff[x];
+          v = in ? static_cast<uint32_t>(x) : v;
+          base = in ? woff[x] : base;
+        }
+        const uint32_t at = v * kWaveStage + (i - base);
+        __builtin_amdgcn_raw_buffer_store_b32(hist[at], prs, i * 4, 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(scol[at]), pcs, i * 2, 0, kCoherent);
+      }
+    } else {
+      __syncthreads();  // the regions are rewritten
+      uint32_t at = woff[wv];
+#pragma unroll
+      for (int u = 0; u < E; ++u) {
+        const bool hit = kv[u] >= lb;
+        const uint64_t m = __ballot(hit);
+        if (m != 0u) {
+          const uint32_t a = at + lanes_below(m);
+          if (hit) {
+            hist[a] = kv[u];
+            scol[a] = static_cast<uint16_t>(e0 + u * kWave);
+          }
+          at += static_cast<uint32_t>(__popcll(m));
+        }
+      }
+      __syncthreads();
+      for (uint32_t i = static_cast<uint32_t>(tid); i < total; i += BLOCK) {
+        __builtin_amdgcn_raw_buffer_store_b32(hist[i], prs, i * 4, 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(scol[i]), pcs, i * 2, 0, kCoherent);
+      }
     }
   }
   if (tid == 0) {
