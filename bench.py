@@ -7,7 +7,10 @@ last-level cache) is touched between two uses of one copy, so that no step
 finds its input in a cache (2 copies for the prefill batch, 21 for the
 long-context batch).  The timed region is K launches back to back between two
 HIP events on the launch stream; a separate pass with an event pair around
-each launch gives the spread of single launches.  Prints one JSON line.
+each launch gives the spread of single launches.  For context the line also
+carries `read_ceiling`: a plain max (torch.amax) over the same bytes and input
+copies (rows cut into pieces when there are few), timed the same way, i.e.
+what a simple streaming read of the batch reaches on this GPU.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload prefill]
 """
@@ -158,6 +161,40 @@ def time_workload(w, steps: int, warmup: int, copies: int = 2):
     return total_ms, per_launch_ms, wall
 
 
+def read_ceiling(w, steps: int, warmup: int, copies: int):
+    """A plain streaming read of the same bytes for context: torch.amax over
+    the batch's full strides, on the same rotation of cold input copies,
+    timed like the top-k launches (back to back between two events).  Rows
+    are cut into f pieces (f a power of two dividing the stride) until there
+    are at least 2048 pieces, none below 1024 entries, so that a batch of a
+    few long rows still spreads over the whole GPU."""
+    dev = torch.device("cuda:0")
+    f = 1
+    while (w.num_rows * f < 2048 and w.row_stride % (2 * f) == 0
+           and w.row_stride // (2 * f) >= 1024):
+        f *= 2
+    shape = (w.num_rows * f, w.row_stride // f)
+    bufs = [w.flat.to(dev).as_strided(shape, (shape[1], 1)) for _ in range(copies)]
+    for i in range(warmup):
+        torch.amax(bufs[i % copies], dim=1)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(steps):
+        torch.amax(bufs[i % copies], dim=1)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    us = t_start.elapsed_time(t_end) / steps * 1e3
+    nbytes = 4.0 * w.num_rows * w.row_stride
+    del bufs
+    return {"kernel": "torch.amax(dim=1) over the full row strides", "view": list(shape),
+            "us_per_launch": us,
+            "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
+            "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
 def calibrate_copy() -> None:
     """A plain copy of known size, to scale the HBM byte counters by."""
     n = 1 << 28
@@ -251,6 +288,7 @@ def main() -> None:
                                "rows_per_s": w2.num_rows / (t2 / args.steps * 1e-3),
                                "achieved_gbs": b2 / (m2 * 1e-3) / 1e9,
                                "frac": b2 / (m2 * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    result["read_ceiling"] = read_ceiling(w, args.steps, args.warmup, copies)
     print(json.dumps(result), flush=True)
 
 

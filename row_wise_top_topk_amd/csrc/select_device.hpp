@@ -205,47 +205,11 @@ __device__ __forceinline__ void count_digit_agg(ForEach for_each, const Prefix& 
   }
 }
 
-// Finds the bucket b holding the need-th largest entry of a histogram of nb
-// bins (nb a power of two): the largest b with sum(hist[b..nb)) >= need.
-// Thread t owns a group of adjacent bins counted from the top; a workgroup
-// prefix sum over the groups gives each group the number of entries above
-// it, and the one group where that count crosses `need` walks its bins.
+// Finds the bucket b holding the need-th largest entry of a histogram of NB
+// bins (NB a power of two): the largest b with sum(hist[b..NB)) >= need.
 // Result in LDS: res[0] bucket, res[1] entries in higher buckets, res[2]
-// entries in the bucket.
-template <int BLOCK>
-__device__ __forceinline__ void find_bucket(const uint32_t* hist, int nb, uint32_t need,
-                                            uint32_t* lds_scan, uint32_t* res) {
-  const int tid = threadIdx.x;
-  const int bpt = nb >= BLOCK ? nb / BLOCK : 1;
-  const int groups = nb / bpt;
-  const int top = nb - tid * bpt;  // this thread's bins: [top - bpt, top)
-  uint32_t s = 0;
-  if (tid < groups) {
-    for (int i = 0; i < bpt; ++i) s += hist[top - 1 - i];
-  }
-  uint32_t v[1] = {s}, tot[1];
-  block_inclusive_sum<BLOCK, 1>(v, tot, lds_scan);
-  const uint32_t incl = v[0];
-  const uint32_t excl = incl - s;
-  if (tid < groups && excl < need && incl >= need) {
-    uint32_t run = excl;
-    for (int i = 0; i < bpt; ++i) {
-      const int bin = top - 1 - i;
-      const uint32_t h = hist[bin];
-      if (run + h >= need) {
-        res[0] = static_cast<uint32_t>(bin);
-        res[1] = run;
-        res[2] = h;
-        break;
-      }
-      run += h;
-    }
-  }
-  __syncthreads();
-}
-
-// The same search done by the calling wavefront alone (the other wavefronts
-// of the workgroup need not take part), in two levels: lane l first sums a
+// entries in the bucket.  Done by the calling wavefront alone (the other
+// wavefronts of the workgroup need not take part), in two levels: lane l first sums a
 // group of NB/64 adjacent bins (group l counted from the top, read with
 // 16-byte LDS loads), a wavefront prefix sum finds the group holding the
 // need-th entry, and then lane i reads bin i of that group and a second

@@ -1129,8 +1129,8 @@ topk_split_kernel(Params p) {
 // estimates, from a sample of its own chunk, a bound below which no entry of
 // the row's top k is expected: with ns sample entries of a chunk of a row of
 // length L, k*ns/L of them are expected at or above the row's threshold, and
-// the bound is the first-digit bin edge where the sample's count from the top
-// reaches ceil(3 k ns / 2L) + 16, far beyond that expectation.  The chunk's
+// the bound is the sample entry (to 22 key bits) where the sample's count from
+// the top reaches ceil(3 k ns / 2L) + 16, far beyond that expectation.  The chunk's
 // entries at or above its bound go to the row's workspace in column order,
 // with the chunk's count and bound.  The last workgroup of the row to arrive
 // (a device-scope counter, which it then resets) gathers the chunks'
@@ -1164,10 +1164,12 @@ __host__ __device__ constexpr size_t chunk_row_bytes(int G) {
          static_cast<size_t>(G) * kChunkCap * 6;
 }
 
-// The union of the chunks' candidates in registers: thread t holds entries
-// t, t + BLOCK, t + 2*BLOCK, ... of the union (which is in column order);
-// unused entries have key 0.  An entry's column is its chunk's first column
-// plus the offset published with it.
+// The union of the chunks' candidates in registers: thread t holds four
+// groups of four consecutive union entries, group q being union entries
+// 4*(q*BLOCK + t) .. +3, so entry u = 4q + j of the thread is union entry
+// 4*(q*BLOCK + t) + j (the union is in column order); unused entries have
+// key 0.  An entry's column is its chunk's first column plus the 16-bit
+// offset published with it, which is read only where a column is used.
 template <int CHUNK>
 struct UnionList {
   uint32_t key[kUnionPerThread];

@@ -1,6 +1,6 @@
-// Wavefront-64 and workgroup primitives for gfx950 (CDNA4).
+// Wavefront-64 primitives for gfx950 (CDNA4).
 //
-// Prefix sums across a 64-lane wavefront and across a workgroup, used by the
+// Prefix sums, sums and maxima across a 64-lane wavefront, used by the
 // radix-select kernels for the histogram suffix scan (finding the threshold
 // bucket) and for ordered compaction of the selected indices.
 #pragma once
@@ -51,50 +51,6 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 // Sum over the lanes of one wavefront (every lane gets it).
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_inclusive_sum(v)), 63));
-}
-
-// LDS words block_inclusive_sum<BLOCK, NV> needs.
-template <int BLOCK, int NV>
-constexpr int scan_lds_words() {
-  return NV * (BLOCK / kWave) + NV;
-}
-
-// Inclusive prefix sums of NV independent per-thread values across a
-// workgroup of BLOCK threads (BLOCK a multiple of 64, at most 1024).  On
-// return v[i] holds the inclusive prefix of value i and tot[i] its workgroup
-// total.  Each wavefront scans its lanes; wavefront 0 then scans the
-// wavefront totals and leaves each wavefront's offset in LDS, so a thread
-// reads one offset per value instead of every wavefront's total.  Contains
-// three workgroup barriers; every thread of the workgroup must call it.
-template <int BLOCK, int NV>
-__device__ __forceinline__ void block_inclusive_sum(uint32_t (&v)[NV], uint32_t (&tot)[NV],
-                                                    uint32_t* lds) {
-  constexpr int NW = BLOCK / kWave;
-  static_assert(NW >= 1 && NW <= kWave, "workgroup of 64..4096 threads");
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    v[i] = wave_inclusive_sum(v[i]);
-    if (lane == kWave - 1) lds[i * NW + w] = v[i];
-  }
-  __syncthreads();
-  if (w == 0) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const uint32_t x = lane < NW ? lds[i * NW + lane] : 0u;
-      const uint32_t incl = wave_inclusive_sum(x);
-      if (lane < NW) lds[i * NW + lane] = incl - x;
-      if (lane == NW - 1) lds[NV * NW + i] = incl;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    v[i] += lds[i * NW + w];
-    tot[i] = lds[NV * NW + i];
-  }
-  __syncthreads();
 }
 
 }  // namespace mitopk
