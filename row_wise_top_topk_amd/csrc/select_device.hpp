@@ -389,6 +389,53 @@ __device__ __forceinline__ Prefix rounds_local(const Src& src, Prefix p, uint32_
   return p;
 }
 
+// The last step when the bucket of key prefix kp (the top 32 - sh key bits)
+// holds at most 64 entries: they are gathered into LDS (lds[2i] key,
+// lds[2i + 1] column, in any order; res[3] counts them and must be zero on
+// entry), and one wavefront ranks each against the others by the composite
+// (key, then lower column first); the entry of rank need - 1 is the last one
+// selected.  Returns the prefix that selects exactly the need entries of the
+// bucket: key >= T (32 bits) when no entry with key T falls below it, else
+// the whole composite.  Two workgroup barriers; every thread must call it.
+template <int BLOCK, class Src>
+__device__ __forceinline__ Prefix finish_small(const Src& src, uint32_t kp, int sh, uint32_t need,
+                                               int ib, uint32_t* lds, uint32_t* res) {
+  src([&](uint32_t key, int32_t j) {
+    if (key != 0u && (key >> sh) == kp) {
+      const uint32_t at = atomicAdd(&res[3], 1u);
+      lds[2 * at] = key;
+      lds[2 * at + 1] = static_cast<uint32_t>(j);
+    }
+  });
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const uint32_t n = res[3];
+    const uint32_t lane = __lane_id();
+    const uint32_t k = lane < n ? lds[2 * lane] : 0u;
+    const uint32_t j = lane < n ? lds[2 * lane + 1] : 0u;
+    uint32_t rank = 0;  // entries of the bucket ordered before this one
+    for (uint32_t i = 0; i < n; ++i) {
+      const uint32_t ki = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(k), static_cast<int>(i)));
+      const uint32_t ji = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(j), static_cast<int>(i)));
+      rank += (ki > k || (ki == k && ji < j)) ? 1u : 0u;
+    }
+    const uint64_t m = __ballot(lane < n && rank == need - 1u);
+    const int tl = __ffsll(static_cast<unsigned long long>(m)) - 1;
+    const uint32_t T = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(k), tl));
+    const uint32_t jt = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(j), tl));
+    const uint64_t tie_below = __ballot(lane < n && k == T && rank >= need);
+    if (lane == 0) {
+      res[0] = T;
+      res[1] = jt;
+      res[2] = tie_below != 0 ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  const uint32_t T = res[0], jt = res[1];
+  if (res[2] == 0u) return Prefix{32, T, 0u};
+  return Prefix{32 + ib, T, ((1u << ib) - 1u) - jt};
+}
+
 // Radix rounds for entries whose keys all lie in [lo, hi] (entries outside
 // the row carry key 0).  The first round histograms the key bits just below
 // the ones every key in [lo, hi] shares: the shift s is the smallest that
@@ -396,8 +443,9 @@ __device__ __forceinline__ Prefix rounds_local(const Src& src, Prefix p, uint32_
 // with key >> s == (lo >> s) + i, so its bucket is an ordinary key prefix of
 // 32 - s bits.  When the keys are confined to a narrow range (a filtered
 // list), that one round resolves as many bits as two or three full-range
-// digits and spreads the entries over many bins.  Later rounds continue with
-// rounds_local.  Returns the final prefix.
+// digits and spreads the entries over many bins.  A bucket of at most 64
+// entries is then finished by finish_small, a larger one by rounds_local.
+// res[3] is overwritten.  Returns the final prefix.
 template <int BLOCK, class Src>
 __device__ __forceinline__ Prefix rounds_window(const Src& src, uint32_t lo, uint32_t hi,
                                                 uint32_t need, int ib, uint32_t* hist,
@@ -411,12 +459,14 @@ __device__ __forceinline__ Prefix rounds_window(const Src& src, uint32_t lo, uin
     if (key != 0u) atomicAdd(&hist[(key >> s) - base], 1u);
   });
   __syncthreads();
+  if (threadIdx.x == 0) res[3] = 0u;  // finish_small's counter (visible after the search's barrier)
   find_bucket_block<BLOCK, kFirstBins>(hist, [need](uint32_t) { return need; }, res, wt);
   __syncthreads();
   const uint32_t b = res[0], gt = res[1], cnt = res[2];
   need -= gt;
   const Prefix p{32 - s, base + b, 0u};
   if (cnt == need) return p;
+  if (cnt <= static_cast<uint32_t>(kWave)) return finish_small<BLOCK>(src, base + b, s, need, ib, hist, res);
   return rounds_local<BLOCK>(src, p, need, ib, hist, res, wt);
 }
 
