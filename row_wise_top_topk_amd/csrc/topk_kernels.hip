@@ -1703,7 +1703,7 @@ topk_chunks_kernel(Params p) {
           __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(0), crs, un.sat[u] * 2, 0, kCoherent);
         }
     }
-    __syncthreads();
+    if (!done) __syncthreads();  // the streamed selection reuses the LDS
   }
   if (!done) select_row_streamed<BLOCK>(row_ptr, L, p.k, out_row, hist, wtot, res);
   if (!exact_ok) {

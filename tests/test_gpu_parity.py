@@ -195,6 +195,30 @@ def test_chunks_long_workload_leaves_workspace_zero():
             assert int(ws.count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("ties", [3, 10, 40, 200])
+@pytest.mark.parametrize("stride,k,path", [(32768, 2048, "auto"), (300032, 2048, "chunks"),
+                                           (60000, 1024, "chunks"), (20000, 512, "auto")])
+def test_ties_straddle_the_threshold(stride, k, path, ties):
+    # `ties` entries ranked around the k-th all take the k-th value, so the
+    # threshold key is tied across the cut: the lowest columns among the
+    # ties are selected.  Few ties stay inside a small last bucket (finished
+    # by one wavefront), many go through further radix rounds.
+    rows = 4
+    rng = np.random.default_rng(stride * 7 + ties)
+    x = rng.standard_normal((rows, stride)).astype(np.float32)
+    for r in range(rows):
+        order = np.argsort(-x[r], kind="stable")
+        v = x[r, order[k - 1]]
+        lo = k - 1 - ties // 2
+        x[r, order[lo:lo + ties]] = v
+    flat = torch.from_numpy(x.reshape(-1))
+    lengths = torch.full((rows,), stride, dtype=torch.int32)
+    w = workloads.Workload("ties", flat, stride, lengths, rows, k)
+    ref = expected(w)
+    got = run_gpu(w, path=path)
+    assert np.array_equal(got, ref)
+
+
 def test_chunks_cluster_in_one_chunk():
     # one chunk holds a block of 3000 equal high values: its count exceeds the
     # last workgroup's fixed window, so the union is gathered through the
