@@ -10,7 +10,8 @@ HIP events on the launch stream; a separate pass with an event pair around
 each launch gives the spread of single launches.  For context the line also
 carries `read_ceiling`: a plain max (torch.amax) over the same bytes and input
 copies (rows cut into pieces when there are few), timed the same way, i.e.
-what a simple streaming read of the batch reaches on this GPU.  Prints one JSON line.
+what a simple streaming read of the batch reaches on this GPU, and
+`warm_cache`: the same launches on one reused input copy.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload prefill]
 """
@@ -86,10 +87,16 @@ def cpu_baseline(w, max_rows: int) -> dict:
     with ctx.Pool(cores) as pool:
         done = sum(pool.map(_oracle_rows, parts))
     dt = time.perf_counter() - t0
+    one = rows[:512]
+    t1 = time.perf_counter()
+    n1 = _oracle_rows(one)
+    d1 = time.perf_counter() - t1
     return {"value": done / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
             "sample": f"first {done} rows of the {w.name} workload, one pass, "
                       f"numpy stable argsort per row across a {cores}-process pool "
-                      f"({dt:.2f} s wall)"}
+                      f"({dt:.2f} s wall)",
+            "value_1core": n1 / d1,
+            "sample_1core": f"first {n1} rows on one core ({d1:.2f} s)"}
 
 
 # ---------------------------------------------------------------- GPU leg
@@ -209,8 +216,8 @@ def calibrate_copy() -> None:
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--secondary", default="long",
                     help="a second workload timed for context ('' to skip)")
@@ -262,6 +269,8 @@ def main() -> None:
         "data": "synthetic",
         "config": {"workload": DESCRIPTIONS[args.workload], "rows": w.num_rows,
                    "row_stride": w.row_stride, "k": w.k, "valid_elements": w.valid_elements,
+                   "rows_with_length_below_k": int((w.lengths.to(torch.int64).clamp(0, w.row_stride)
+                                                    < w.k).sum()),
                    "algorithmic_bytes": alg_bytes, "input_copies": copies,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -288,7 +297,14 @@ def main() -> None:
                                "rows_per_s": w2.num_rows / (t2 / args.steps * 1e-3),
                                "achieved_gbs": b2 / (m2 * 1e-3) / 1e9,
                                "frac": b2 / (m2 * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    result["read_ceiling"] = read_ceiling(w, args.steps, args.warmup, copies)
+    warm_ms, _, _ = time_workload(w, args.steps, args.warmup, copies=1)
+    result["warm_cache"] = {"input_copies": 1, "launch_us_mean": warm_ms / args.steps * 1e3,
+                            "achieved_gbs": alg_bytes / (warm_ms / args.steps * 1e-3) / 1e9,
+                            "note": "one input copy reused: parts of it may be served from the caches"}
+    rc = read_ceiling(w, args.steps, args.warmup, copies)
+    rc["topk_over_read_time"] = avg_launch_ms * 1e3 / rc["us_per_launch"]
+    rc["topk_gbs_over_read_gbs"] = achieved / rc["gbs"]
+    result["read_ceiling"] = rc
     print(json.dumps(result), flush=True)
 
 
