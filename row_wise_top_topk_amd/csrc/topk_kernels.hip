@@ -1256,8 +1256,14 @@ struct RowStream {
   }
 };
 
-// Exact selection of a whole row streamed from memory by one workgroup:
-// radix rounds, then, block by block, an ordered emission.
+// Exact selection of a whole row streamed from memory by one workgroup.
+// Radix rounds over the key digits (12, 10, 10 bits) run until the bucket
+// holding the k-th entry is taken whole or the threshold key T is known;
+// then, block by block, an ordered emission.  When only part of T's bucket
+// is taken, the emission takes every entry above T and the first `need`
+// entries equal to T in column order (the lowest columns among the ties),
+// counting the ties before each entry as it goes, so ties cost no rounds
+// over index digits.
 template <int BLOCK>
 __device__ __forceinline__ void select_row_streamed(const float* row, int L, int k, int32_t* out_row,
                                                  uint32_t* hist, uint32_t* wtot, uint32_t* res) {
@@ -1266,29 +1272,96 @@ __device__ __forceinline__ void select_row_streamed(const float* row, int L, int
   const int ib = index_bits(L);
   const uint32_t rmask = (1u << ib) - 1u;
   const uint32_t kk = static_cast<uint32_t>(k);
-  const Prefix pf = rounds_local<BLOCK>(src, Prefix{0, 0u, 0u}, kk, ib, hist, res, wtot);
-  with_pred(pf, ib, rmask, [&](const auto& pred) {
-    uint32_t out_base = 0;
-    src.blocks([&](const uint32_t (&buf)[kChunkPos], int e0) {
-      uint32_t n = 0;
+  const int tid = static_cast<int>(threadIdx.x);
+  uint32_t need = kk;
+  Prefix pf{0, 0u, 0u};
+  bool whole = false;  // the last bucket is taken whole
+  while (pf.bits < 32) {
+    const int d = digit_bits(pf.bits, ib);
+    const int nb = 1 << d;
+    for (int i = tid; i < nb; i += BLOCK) hist[i] = 0;
+    __syncthreads();
+    src.count(pf, d, ib, rmask, hist);
+    __syncthreads();
+    const auto fixed = [need](uint32_t) { return need; };
+    if (d == kFirstBits) {
+      find_bucket_block<BLOCK, kFirstBins>(hist, fixed, res, wtot);
+    } else {
+      find_bucket_block<BLOCK, kNextBins>(hist, fixed, res, wtot);
+    }
+    __syncthreads();
+    const uint32_t b = res[0], gt = res[1], cnt = res[2];
+    need -= gt;
+    pf = extend(pf, d, b);
+    if (cnt == need) {
+      whole = true;
+      break;
+    }
+  }
+  uint32_t out_base = 0;
+  if (whole) {
+    with_pred(pf, ib, rmask, [&](const auto& pred) {
+      src.blocks([&](const uint32_t (&buf)[kChunkPos], int e0) {
+        uint32_t n = 0;
 #pragma unroll
-      for (int u = 0; u < kChunkPos; ++u) n += pred.ge(buf[u], e0 + u * kWave) ? 1u : 0u;
-      uint32_t pos = out_base + wave_offset<BLOCK>(wave_sum(n), wtot);
-      uint32_t block_total = 0;
+        for (int u = 0; u < kChunkPos; ++u) n += pred.ge(buf[u], e0 + u * kWave) ? 1u : 0u;
+        uint32_t pos = out_base + wave_offset<BLOCK>(wave_sum(n), wtot);
+        uint32_t block_total = 0;
 #pragma unroll
-      for (int i = 0; i < NW; ++i) block_total += wtot[i];
+        for (int i = 0; i < NW; ++i) block_total += wtot[i];
 #pragma unroll
-      for (int u = 0; u < kChunkPos; ++u) {
-        const int32_t j = e0 + u * kWave;
-        const bool sel = pred.ge(buf[u], j);
-        const uint64_t m = __ballot(sel);
-        const uint32_t at = pos + lanes_below(m);
-        if (sel && at < kk) out_row[at] = j;
-        pos += static_cast<uint32_t>(__popcll(m));
-      }
-      out_base += block_total;
-      __syncthreads();  // wtot is reused
+        for (int u = 0; u < kChunkPos; ++u) {
+          const int32_t j = e0 + u * kWave;
+          const bool sel = pred.ge(buf[u], j);
+          const uint64_t m = __ballot(sel);
+          const uint32_t at = pos + lanes_below(m);
+          if (sel && at < kk) out_row[at] = j;
+          pos += static_cast<uint32_t>(__popcll(m));
+        }
+        out_base += block_total;
+        __syncthreads();  // wtot is reused
+      });
     });
+    return;
+  }
+  // T = pf.kp (the whole key); `need` entries equal to T are taken.  In a
+  // block, column order is (wavefront, position, lane).
+  const uint32_t T = pf.kp;
+  uint32_t tie_run = 0;  // entries equal to T in the earlier blocks
+  src.blocks([&](const uint32_t (&buf)[kChunkPos], int e0) {
+    uint32_t tw = 0;
+#pragma unroll
+    for (int u = 0; u < kChunkPos; ++u) tw += static_cast<uint32_t>(__popcll(__ballot(buf[u] == T)));
+    uint32_t tr = tie_run + wave_offset<BLOCK>(tw, wtot);
+    uint32_t tie_block = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) tie_block += wtot[i];
+    __syncthreads();  // wtot is reused
+    uint32_t n = 0, selm = 0;
+#pragma unroll
+    for (int u = 0; u < kChunkPos; ++u) {
+      const bool tie = buf[u] == T;
+      const uint64_t m = __ballot(tie);
+      const bool sel = buf[u] > T || (tie && tr + lanes_below(m) < need);
+      selm |= sel ? (1u << u) : 0u;
+      n += sel ? 1u : 0u;
+      tr += static_cast<uint32_t>(__popcll(m));
+    }
+    uint32_t pos = out_base + wave_offset<BLOCK>(wave_sum(n), wtot);
+    uint32_t block_total = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) block_total += wtot[i];
+#pragma unroll
+    for (int u = 0; u < kChunkPos; ++u) {
+      const bool sel = ((selm >> u) & 1u) != 0u;
+      const uint64_t m = __ballot(sel);
+      const uint32_t at = pos + lanes_below(m);
+      if (sel && at < kk) out_row[at] = e0 + u * kWave;
+      pos += static_cast<uint32_t>(__popcll(m));
+    }
+    out_base += block_total;
+    tie_run += tie_block;
+    __syncthreads();  // wtot is reused
   });
 }
 
