@@ -1490,12 +1490,14 @@ topk_chunks_kernel(Params p) {
   // wavefront stages its candidates in its own region of kWaveStage LDS
   // entries (keys in the histogram's words, column offsets in scol) while
   // counting them; the wavefronts' counts then place the regions one after
-  // another, and consecutive threads write the list out.  A wavefront with
-  // more candidates than its region sends the chunk through the same steps
-  // with positions counted first (one region for the whole chunk).
+  // another, and consecutive threads write the list out.  A chunk whose
+  // ties at the bound are cut (below), or a wavefront with more candidates
+  // than its region holds, goes through the same steps with positions
+  // counted first.
   constexpr uint32_t kWaveStage = kChunkCap / NW;
   const uint32_t wv = wave_id();
   uint32_t pos = 0;  // this wavefront's candidates so far (uniform)
+  uint32_t tw = 0;   // ... and those equal to the bound
 #pragma unroll
   for (int u = 0; u < E; ++u) {
     const bool hit = kv[u] >= lb;
@@ -1507,9 +1509,13 @@ topk_chunks_kernel(Params p) {
         scol[wv * kWaveStage + at] = static_cast<uint16_t>(e0 + u * kWave);
       }
       pos += static_cast<uint32_t>(__popcll(m));
+      tw += static_cast<uint32_t>(__popcll(__ballot(kv[u] == lb)));
     }
   }
-  if (__lane_id() == 0) wtot[wv] = pos;
+  if (__lane_id() == 0) {
+    wtot[wv] = pos;
+    wq[wv] = tw;
+  }
   __syncthreads();
   uint32_t woff[NW + 1];
   woff[0] = 0;
@@ -1520,13 +1526,26 @@ topk_chunks_kernel(Params p) {
     woff[v + 1] = woff[v] + c;
     spill |= c > kWaveStage;
   }
-  const uint32_t total = woff[NW];
+  uint32_t total = woff[NW];
+  // Of the chunk's entries equal to its bound, only the first k - A in
+  // column order (A: its entries above the bound) can be selected: ties are
+  // taken lowest column first and k entries at most, and if the row's
+  // threshold is below the bound all of the chunk's entries at or above it
+  // are selected, so there are at most k of them.  Long runs of ties (more
+  // than a wavefront's worth) beyond that allowance are cut.
+  uint32_t ties = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) ties += wq[v];
+  const uint32_t above = total - ties;
+  const uint32_t allowed = above < kk ? min(ties, kk - above) : 0u;
+  const bool cut = allowed < ties && ties > static_cast<uint32_t>(kWave);
+  const uint32_t limit = cut ? allowed : ties;
   const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
       ckeys + static_cast<size_t>(g) * kChunkCap * 4, 0, kChunkCap * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t pcs = __builtin_amdgcn_make_buffer_rsrc(
       ccols + static_cast<size_t>(g) * kChunkCap * 2, 0, kChunkCap * 2, 0x00020000);
-  if (total <= static_cast<uint32_t>(kChunkCap)) {  // else the row falls back: publish the count only
-    if (!spill) {
+  if (!spill && !cut) {
+    if (total <= static_cast<uint32_t>(kChunkCap)) {  // else the row falls back: publish the count only
       for (uint32_t i = static_cast<uint32_t>(tid); i < total; i += BLOCK) {
         uint32_t v = 0, base = 0;  // the region holding list entry i
 #pragma unroll
@@ -1539,21 +1558,41 @@ topk_chunks_kernel(Params p) {
         __builtin_amdgcn_raw_buffer_store_b32(hist[at], prs, i * 4, 0, kCoherent);
         __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(scol[at]), pcs, i * 2, 0, kCoherent);
       }
-    } else {
+    }
+  } else {
+    // positions counted first: the entries above the bound and the first
+    // `limit` ties, one list for the whole chunk
+    uint32_t tp = 0, kp = 0, my_tp = 0, my_kp = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const uint32_t t_v = wq[v];
+      const uint32_t keep_t = tp >= limit ? 0u : min(t_v, limit - tp);
+      if (static_cast<uint32_t>(v) == wv) {
+        my_tp = tp;
+        my_kp = kp;
+      }
+      tp += t_v;
+      kp += wtot[v] - t_v + keep_t;
+    }
+    total = kp;
+    if (total <= static_cast<uint32_t>(kChunkCap)) {  // else the row falls back: publish the count only
       __syncthreads();  // the regions are rewritten
-      uint32_t at = woff[wv];
+      uint32_t at = my_kp, tr = my_tp;
 #pragma unroll
       for (int u = 0; u < E; ++u) {
-        const bool hit = kv[u] >= lb;
-        const uint64_t m = __ballot(hit);
-        if (m != 0u) {
-          const uint32_t a = at + lanes_below(m);
-          if (hit) {
-            hist[a] = kv[u];
-            scol[a] = static_cast<uint16_t>(e0 + u * kWave);
+        const bool tie = kv[u] == lb;
+        const uint64_t mt = __ballot(tie);
+        const bool keep = kv[u] >= lb && (!tie || tr + lanes_below(mt) < limit);
+        const uint64_t mk = __ballot(keep);
+        if (mk != 0u) {
+          const uint32_t a2 = at + lanes_below(mk);
+          if (keep) {
+            hist[a2] = kv[u];
+            scol[a2] = static_cast<uint16_t>(e0 + u * kWave);
           }
-          at += static_cast<uint32_t>(__popcll(m));
+          at += static_cast<uint32_t>(__popcll(mk));
         }
+        tr += static_cast<uint32_t>(__popcll(mt));
       }
       __syncthreads();
       for (uint32_t i = static_cast<uint32_t>(tid); i < total; i += BLOCK) {
