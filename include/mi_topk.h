@@ -133,6 +133,18 @@ int topk_plan_describe(int64_t num_rows, int64_t row_stride, int32_t k, int32_t 
                        int32_t chunks, int64_t* info);
 
 /*
+ * The same description for a device given by its properties instead of the
+ * current one: `cus` compute units, `coop` nonzero if it supports cooperative
+ * launches, `split_per_cu` co-resident workgroups of the cooperative split
+ * kernel per compute unit.  Makes no HIP call (the host planning alone, e.g.
+ * for tests on a machine without a GPU).  Returns a status code, as
+ * topk_plan_describe() (MI_TOPK_EINVAL also for cus < 1 or split_per_cu < 0).
+ */
+int topk_plan_describe_for(int64_t num_rows, int64_t row_stride, int32_t k, int32_t path,
+                           int32_t chunks, int32_t cus, int32_t coop, int32_t split_per_cu,
+                           int64_t* info);
+
+/*
  * Diagnostic: the order-preserving key the kernels give each fp32 value
  * (x < y implies key(x) < key(y); -0.0 and +0.0 share a key; every value,
  * NaN included, maps to a key >= 1).  in and out are device arrays of n

@@ -56,6 +56,8 @@ def load_library() -> ctypes.CDLL:
         lib.topk_indices_path.restype = ctypes.c_int
         lib.topk_plan_describe.argtypes = [i64, i64, i32, i32, i32, ctypes.POINTER(i64)]
         lib.topk_plan_describe.restype = ctypes.c_int
+        lib.topk_plan_describe_for.argtypes = [i64, i64, i32, i32, i32, i32, i32, i32, ctypes.POINTER(i64)]
+        lib.topk_plan_describe_for.restype = ctypes.c_int
         lib.topk_status_string.argtypes = [ctypes.c_int]
         lib.topk_status_string.restype = ctypes.c_char_p
         lib.topk_debug_keys.argtypes = [vp, vp, i64, vp]
@@ -90,6 +92,19 @@ def plan_describe(num_rows: int, row_stride: int, k: int, path="auto", chunks: i
     info = (ctypes.c_int64 * 7)()
     _check(load_library().topk_plan_describe(int(num_rows), int(row_stride), int(k),
                                              _path_id(path), int(chunks), info), "topk_plan_describe")
+    keys = ("path", "block", "elems_per_thread", "chunk", "chunks_per_row", "grid", "workspace_bytes")
+    return dict(zip(keys, (int(v) for v in info)))
+
+
+def plan_describe_for(num_rows: int, row_stride: int, k: int, path="auto", chunks: int = 0,
+                      cus: int = 256, coop: bool = True, split_per_cu: int = 2) -> dict:
+    """plan_describe for a device given by its properties (MI355X: 256 CUs);
+    host planning only, no device is touched."""
+    info = (ctypes.c_int64 * 7)()
+    _check(load_library().topk_plan_describe_for(int(num_rows), int(row_stride), int(k),
+                                                 _path_id(path), int(chunks), int(cus),
+                                                 int(bool(coop)), int(split_per_cu), info),
+           "topk_plan_describe_for")
     keys = ("path", "block", "elems_per_thread", "chunk", "chunks_per_row", "grid", "workspace_bytes")
     return dict(zip(keys, (int(v) for v in info)))
 

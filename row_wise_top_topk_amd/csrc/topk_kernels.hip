@@ -2082,16 +2082,13 @@ MI_TOPK_EXPORT int topk_indices_path(const float* logits, int64_t row_stride, co
                    chunks, stream);
 }
 
-MI_TOPK_EXPORT int topk_plan_describe(int64_t num_rows, int64_t row_stride, int32_t k, int32_t path,
-                                      int32_t chunks, int64_t* info) {
-  int st = check_shape(num_rows, row_stride, k);
-  if (st != MI_TOPK_OK) return st;
-  if (!info || path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_CHUNKS || chunks < 0) return MI_TOPK_EINVAL;
-  DeviceInfo dev;
-  if (device_info(&dev) != hipSuccess) return MI_TOPK_ELAUNCH;
+namespace mitopk {
+namespace {
+int describe(int64_t num_rows, int64_t row_stride, int32_t k, int32_t path, int32_t chunks,
+             const DeviceInfo& dev, int64_t* info) {
   Plan pl;
   const int head_max = (row_stride & 3) == 0 ? 0 : 3;
-  st = make_plan(num_rows, row_stride, k, path, chunks, head_max, dev, &pl);
+  const int st = make_plan(num_rows, row_stride, k, path, chunks, head_max, dev, &pl);
   if (st != MI_TOPK_OK) return st;
   const KindInfo& ki = kKinds[pl.kind];
   info[0] = ki.mode == kModeSplit ? MI_TOPK_PATH_SPLIT
@@ -2104,6 +2101,33 @@ MI_TOPK_EXPORT int topk_plan_describe(int64_t num_rows, int64_t row_stride, int3
   info[5] = pl.grid;
   info[6] = static_cast<int64_t>(pl.ws_bytes);
   return MI_TOPK_OK;
+}
+}  // namespace
+}  // namespace mitopk
+
+MI_TOPK_EXPORT int topk_plan_describe(int64_t num_rows, int64_t row_stride, int32_t k, int32_t path,
+                                      int32_t chunks, int64_t* info) {
+  const int st = check_shape(num_rows, row_stride, k);
+  if (st != MI_TOPK_OK) return st;
+  if (!info || path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_CHUNKS || chunks < 0) return MI_TOPK_EINVAL;
+  DeviceInfo dev;
+  if (device_info(&dev) != hipSuccess) return MI_TOPK_ELAUNCH;
+  return describe(num_rows, row_stride, k, path, chunks, dev, info);
+}
+
+MI_TOPK_EXPORT int topk_plan_describe_for(int64_t num_rows, int64_t row_stride, int32_t k,
+                                          int32_t path, int32_t chunks, int32_t cus, int32_t coop,
+                                          int32_t split_per_cu, int64_t* info) {
+  const int st = check_shape(num_rows, row_stride, k);
+  if (st != MI_TOPK_OK) return st;
+  if (!info || path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_CHUNKS || chunks < 0 || cus < 1 ||
+      split_per_cu < 0)
+    return MI_TOPK_EINVAL;
+  DeviceInfo dev;
+  dev.cus = cus;
+  dev.coop = coop;
+  dev.split_per_cu = split_per_cu;
+  return describe(num_rows, row_stride, k, path, chunks, dev, info);
 }
 
 MI_TOPK_EXPORT const char* topk_status_string(int status) {
