@@ -445,16 +445,20 @@ __device__ __forceinline__ Prefix finish_small(const Src& src, uint32_t kp, int 
 // list), that one round resolves as many bits as two or three full-range
 // digits and spreads the entries over many bins.  A bucket of at most 64
 // entries is then finished by finish_small, a larger one by rounds_local.
-// res[3] is overwritten.  Returns the final prefix.
+// hist_zero: the caller has already zeroed hist[0..kFirstBins) before a
+// workgroup barrier.  res[3] is overwritten.  Returns the final prefix.
 template <int BLOCK, class Src>
 __device__ __forceinline__ Prefix rounds_window(const Src& src, uint32_t lo, uint32_t hi,
                                                 uint32_t need, int ib, uint32_t* hist,
-                                                uint32_t* res, uint32_t* wt) {
+                                                uint32_t* res, uint32_t* wt,
+                                                bool hist_zero = false) {
   int s = 0;
   while ((hi >> s) - (lo >> s) >= static_cast<uint32_t>(kFirstBins)) ++s;
   const uint32_t base = lo >> s;
-  for (int i = threadIdx.x; i < kFirstBins; i += BLOCK) hist[i] = 0;
-  __syncthreads();
+  if (!hist_zero) {  // (uniform) else the caller cleared it before a barrier
+    for (int i = threadIdx.x; i < kFirstBins; i += BLOCK) hist[i] = 0;
+    __syncthreads();
+  }
   src([&](uint32_t key, int32_t) {
     if (key != 0u) atomicAdd(&hist[(key >> s) - base], 1u);
   });

@@ -1156,11 +1156,12 @@ constexpr int kChunkSamples = 16;     // sample positions per thread (the first 
 
 // Row r's block in the workspace (after the header) starts at
 // r * chunk_row_bytes(G): a 256-byte head whose word 0 counts the row's
-// arrived workgroups, then count[G] and bound[G] (rounded to 256 bytes), then
-// the candidates' keys (u32, G lists of kChunkCap) and their column offsets
-// within the chunk (u16, G lists of kChunkCap).
+// arrived workgroups, then count[G], bound[G] and the largest published key
+// kmax[G] (rounded to 256 bytes), then the candidates' keys (u32, G lists of
+// kChunkCap) and their column offsets within the chunk (u16, G lists of
+// kChunkCap).
 __host__ __device__ constexpr size_t chunk_row_bytes(int G) {
-  return 256 + ((8 * static_cast<size_t>(G) + 255) / 256) * 256 +
+  return 256 + ((12 * static_cast<size_t>(G) + 255) / 256) * 256 +
          static_cast<size_t>(G) * kChunkCap * 6;
 }
 
@@ -1439,7 +1440,8 @@ topk_chunks_kernel(Params p) {
   uint32_t* arrived = reinterpret_cast<uint32_t*>(rb);
   uint32_t* counts = reinterpret_cast<uint32_t*>(rb + 256);
   uint32_t* bounds = counts + G;
-  uint8_t* ckeys = rb + 256 + ((8 * static_cast<size_t>(G) + 255) / 256) * 256;  // u32 [G][kChunkCap]
+  uint32_t* kmaxs = bounds + G;
+  uint8_t* ckeys = rb + 256 + ((12 * static_cast<size_t>(G) + 255) / 256) * 256;  // u32 [G][kChunkCap]
   uint8_t* ccols = ckeys + static_cast<size_t>(G) * kChunkCap * 4;                 // u16 [G][kChunkCap]
 
   // sample: the first kChunkSamples positions of each thread
@@ -1498,11 +1500,13 @@ topk_chunks_kernel(Params p) {
   const uint32_t wv = wave_id();
   uint32_t pos = 0;  // this wavefront's candidates so far (uniform)
   uint32_t tw = 0;   // ... and those equal to the bound
+  uint32_t cm = 0;   // the largest key of this thread's candidates
 #pragma unroll
   for (int u = 0; u < E; ++u) {
     const bool hit = kv[u] >= lb;
     const uint64_t m = __ballot(hit);
     if (m != 0u) {  // most positions of a wavefront have no candidate
+      cm = hit ? max(cm, kv[u]) : cm;
       const uint32_t at = pos + lanes_below(m);
       if (hit && at < kWaveStage) {
         hist[wv * kWaveStage + at] = kv[u];
@@ -1512,9 +1516,11 @@ topk_chunks_kernel(Params p) {
       tw += static_cast<uint32_t>(__popcll(__ballot(kv[u] == lb)));
     }
   }
+  cm = wave_max(cm);
   if (__lane_id() == 0) {
     wtot[wv] = pos;
     wq[wv] = tw;
+    wq[NW + wv] = cm;
   }
   __syncthreads();
   uint32_t woff[NW + 1];
@@ -1602,8 +1608,12 @@ topk_chunks_kernel(Params p) {
     }
   }
   if (tid == 0) {
+    uint32_t km = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) km = max(km, wq[NW + v]);
     g_store(&counts[g], total);
     g_store(&bounds[g], lb);
+    g_store(&kmaxs[g], km);
   }
   // arrive; every store above has completed before the counter moves
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1654,13 +1664,17 @@ topk_chunks_kernel(Params p) {
     sk[4 * q + 2] = v.z;
     sk[4 * q + 3] = v.w;
   }
+  // the first window round's histogram is cleared while the keys arrive
+  for (int i = tid; i < kFirstBins; i += BLOCK) hist[i] = 0;
   if (tid < kWave) {
-    // offsets of the chunks' candidates in the packed union, total, bounds
-    uint32_t run = 0, lo = 0xFFFFFFFFu, hi = 0u, bad = 0u, mc = 0u;
+    // offsets of the chunks' candidates in the packed union, total, bounds,
+    // largest key
+    uint32_t run = 0, lo = 0xFFFFFFFFu, hi = 0u, bad = 0u, mc = 0u, km = 0u;
     for (int b0 = 0; b0 < Gr; b0 += kWave) {
       const int c = b0 + tid;
       const uint32_t cnt = c < Gr ? g_load(&counts[c]) : 0u;
       const uint32_t bnd = c < Gr ? g_load(&bounds[c]) : 0u;
+      km = max(km, c < Gr ? g_load(&kmaxs[c]) : 0u);
       const uint32_t incl = wave_inclusive_sum(cnt);
       if (c < Gr) coff[c] = run + incl - cnt;
       run += static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
@@ -1675,6 +1689,7 @@ topk_chunks_kernel(Params p) {
     lo = ~wave_max(~lo);
     bad = wave_max(bad);
     mc = wave_max(mc);
+    km = wave_max(km);
     if (tid == 0) {
       coff[Gr] = run;
       res[5] = run;
@@ -1682,7 +1697,7 @@ topk_chunks_kernel(Params p) {
       res[7] = hi;
       res[8] = bad;
       res[10] = mc;
-      res[3] = 0u;
+      res[11] = km;
     }
   }
   __syncthreads();
@@ -1720,17 +1735,15 @@ topk_chunks_kernel(Params p) {
                     : 0u;
       __syncthreads();  // chunk_of (the histogram's words) is reused
     }
-    uint32_t mx = 0;
+    uint32_t nz = 0;
 #pragma unroll
     for (int u = 0; u < kUnionPerThread; ++u) {
       un.key[u] = sk[u];
-      mx = max(mx, sk[u]);
+      nz |= sk[u];
     }
-    mx = wave_max(mx);
-    if (__lane_id() == 0) atomicMax(&res[3], mx);
     // the keys are consumed before the column loads go out, so no wait
     // for those loads comes before the emission needs them
-    asm volatile("" ::: "memory");
+    asm volatile("" : : "v"(nz) : "memory");
     if (slotted) {
 #pragma unroll
       for (int q = 0; q < kGroups; ++q)
@@ -1744,9 +1757,10 @@ topk_chunks_kernel(Params p) {
       for (int q = 0; q < kGroups; ++q)
         un.offw[q] = u32x2{o[4 * q] | (o[4 * q + 1] << 16), o[4 * q + 2] | (o[4 * q + 3] << 16)};
     }
-    __syncthreads();
-    const uint32_t kmax = res[3];
-    const Prefix pf = rounds_window<BLOCK>(un, min_lb, kmax, kk, ib, hist, res, wtot);
+    const uint32_t kmax = res[11];
+    // slotted: the histogram was cleared before the counts' barrier; packed:
+    // its words held the chunk map, rounds_window clears them
+    const Prefix pf = rounds_window<BLOCK>(un, min_lb, kmax, kk, ib, hist, res, wtot, slotted);
     // every selected key is at least the selected bucket's lower edge
     const uint32_t edge = pf.bits >= 32 ? pf.kp : (pf.kp << (32 - pf.bits));
     if (edge >= max_lb) {
@@ -1832,6 +1846,7 @@ topk_chunks_kernel(Params p) {
   for (int c = tid; c < Gr; c += BLOCK) {
     g_store(&counts[c], 0u);
     g_store(&bounds[c], 0u);
+    g_store(&kmaxs[c], 0u);
   }
 }
 

@@ -3,7 +3,7 @@ on the CPU through topk_plan_describe_for for an MI355X-like device (256
 compute units, cooperative launches, two co-resident split workgroups per
 compute unit).  The expected values are derived by hand from the launch
 layouts: chunked rows of G = ceil(stride / 16384) workgroups with a per-row
-workspace block of 256 + round256(8 G) + G * 4096 * 6 bytes, the split path's
+workspace block of 256 + round256(12 G) + G * 4096 * 6 bytes, the split path's
 78080-byte row block, and one workgroup per row for short rows.
 """
 import pytest
@@ -14,8 +14,9 @@ HEADER = 256
 
 
 def chunk_row_bytes(G: int) -> int:
-    # arrival counter head, counts and bounds, key lists (u32) and column-offset lists (u16)
-    return 256 + ((8 * G + 255) // 256) * 256 + G * 4096 * 4 + G * 4096 * 2
+    # arrival counter head; counts, bounds and largest keys; key lists (u32) and
+    # column-offset lists (u16)
+    return 256 + ((12 * G + 255) // 256) * 256 + G * 4096 * 4 + G * 4096 * 2
 
 
 SPLIT_ROW_BYTES = (2 + 62) * 4 + (4096 + 6 * 1024) * 4 + 1024 * 4 + 4096 * 8
