@@ -121,6 +121,32 @@ def test_random_stress():
         assert_parity(w, got, label=f"trial {trial} rows={rows} stride={stride} k={k} {kind}")
 
 
+def test_random_stress_chunked_path():
+    # the chunked path on random long-row shapes (2 to 25 chunks a row),
+    # random lengths and k, smooth and tied kinds; one workspace for every
+    # call, left all zero each time
+    rng = np.random.default_rng(4321)
+    kinds = ["normal", "bf16", "levels", "equal", "outliers", "ramp"]
+    ws = None
+    for trial in range(36):
+        rows = int(rng.integers(1, 9))
+        stride = int(rng.integers(16385, 400001))
+        k = int(rng.integers(1, 4097))
+        lengths = rng.integers(-2, stride + 3, size=rows)
+        kind = kinds[trial % len(kinds)]
+        w = workloads.make_custom(rows, stride, lengths, k, seed=100 + trial, kind=kind)
+        need = mt.workspace_size(rows, stride, k, path="chunks")
+        if ws is None or ws.numel() < need:
+            ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+        logits, lens = device_view(w)
+        out = mt.topk_indices(logits, lens, k, workspace=ws, path="chunks")
+        torch.cuda.synchronize()
+        w.lengths = w.lengths.clamp(0, stride)
+        label = f"trial {trial} rows={rows} stride={stride} k={k} {kind}"
+        assert_parity(w, out.cpu().numpy(), label=label)
+        assert int(ws.count_nonzero()) == 0, label
+
+
 def test_workspace_reuse_across_calls():
     w = workloads.make_custom(16, 50000, 50000, 1024, seed=9, kind="bf16")
     logits, lengths = device_view(w)
