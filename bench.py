@@ -202,6 +202,32 @@ def read_ceiling(w, steps: int, warmup: int, copies: int):
             "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
+def rows_sweep(name: str, steps: int, warmup: int) -> None:
+    """The workload's rows repeated or cut to several batch sizes, timed like
+    the bench line: a straight-line fit of time against rows separates the
+    per-row (streaming) cost from the fixed cost of a launch (start-up and the
+    last rows' drain).  One JSON line per size, then the fit."""
+    base = workloads.make(name)
+    xs, ys = [], []
+    for rows in (768, 1536, 2304, 3072, 3840, 4608, 5376):
+        reps = -(-rows // base.num_rows)
+        flat = (base.flat.view(base.num_rows, base.row_stride).repeat(reps, 1)[:rows]
+                .reshape(-1).contiguous())
+        lens = base.lengths.repeat(reps)[:rows].contiguous()
+        w = workloads.Workload(f"{name}-rows{rows}", flat, base.row_stride, lens, rows, base.k)
+        t, _, _ = time_workload(w, steps, warmup, copies=input_copies(w))
+        us = t / steps * 1e3
+        xs.append(rows)
+        ys.append(us)
+        print(json.dumps({"rows": rows, "us_per_launch": us,
+                          "achieved_gbs": w.algorithmic_bytes() / (us * 1e-6) / 1e9}), flush=True)
+    slope, icpt = np.polyfit(np.array(xs, dtype=float), np.array(ys), 1)
+    per_row_bytes = base.algorithmic_bytes() / base.num_rows
+    print(json.dumps({"fit": "us = intercept + slope * rows", "intercept_us": icpt,
+                      "slope_ns_per_row": slope * 1e3,
+                      "marginal_gbs": per_row_bytes / (slope * 1e-6) / 1e9}), flush=True)
+
+
 def calibrate_copy() -> None:
     """A plain copy of known size, to scale the HBM byte counters by."""
     n = 1 << 28
@@ -226,9 +252,14 @@ def main() -> None:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB five times (HBM counter calibration)")
+    ap.add_argument("--rows-sweep", action="store_true",
+                    help="only time the workload at several row counts and fit time against rows")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.rows_sweep:
+        rows_sweep(args.workload, args.steps, args.warmup)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): rows are independent, "
