@@ -124,6 +124,41 @@ int topk_indices_path(const float* logits, int64_t row_stride, const int32_t* le
                       hipStream_t stream);
 
 /*
+ * topk_indices() with the index transform that follows the selection on a
+ * paged KV cache applied as the output is written (the pages' kernels pass
+ * their output through a transform as they store it: the report on SGLang
+ * PR #34167, section 关键源码片段, `problem_transform`; the page table and
+ * block size are those the C128A metadata builder takes: "[DSv4 Perf]
+ * Adaptive topk width for dsv4, making #50004 back", section Test/Perf).
+ * A selected column j of row i is written as the KV-cache slot
+ *     block_table[r * block_table_stride + j / page_size] * page_size
+ *       + j % page_size,    r = row_to_req ? row_to_req[i] : i;
+ * -1 padding stays -1, and the slots keep the columns' ascending order.
+ *   block_table         device int32, a row of page numbers per request; row
+ *                       r must hold ceil(L_i / page_size) valid entries for
+ *                       every row i of request r (not checked); 4-byte aligned.
+ *   block_table_stride  entries between two requests' rows (>= 0).
+ *   page_size           columns per page (>= 1; powers of two take shifts).
+ *   row_to_req          device int32 [num_rows], or NULL for row i = request i.
+ * The slot values must fit int32.  Everything else, the workspace included,
+ * as topk_indices() / topk_indices_path().  Returns a status code
+ * (MI_TOPK_EINVAL also for a NULL block_table, page_size < 1, a negative
+ * stride or a misaligned table or map).
+ */
+int topk_indices_paged(const float* logits, int64_t row_stride, const int32_t* lengths,
+                       int64_t num_rows, int32_t k, int32_t* out, void* workspace,
+                       size_t workspace_bytes, const int32_t* block_table,
+                       int64_t block_table_stride, int32_t page_size,
+                       const int32_t* row_to_req, hipStream_t stream);
+
+int topk_indices_paged_path(const float* logits, int64_t row_stride, const int32_t* lengths,
+                            int64_t num_rows, int32_t k, int32_t* out, void* workspace,
+                            size_t workspace_bytes, const int32_t* block_table,
+                            int64_t block_table_stride, int32_t page_size,
+                            const int32_t* row_to_req, int32_t path, int32_t chunks,
+                            hipStream_t stream);
+
+/*
  * Describe the launch topk_indices_path() would make, without launching:
  * writes up to 7 int64 values to `info` (path, block threads, elements per
  * thread, chunk elements, chunks per row, grid workgroups, workspace bytes)

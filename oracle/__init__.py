@@ -8,6 +8,7 @@ from .topk_oracle import (  # noqa: F401
     check_row,
     is_untied,
     oracle_topk,
+    oracle_page_slots,
     oracle_topk_row,
     row_view,
 )

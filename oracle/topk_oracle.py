@@ -32,6 +32,16 @@ What it computes (the plain definition, no radix rounds, no blocking):
 Readings where the pages are silent: output order is free (set semantics;
 ascending order is used here only to give one canonical form); ties are broken
 by lowest index; NaN inside ``L_i`` is outside the contract.
+
+Paged output (``oracle_page_slots``).  On the pages the selection's output
+passes through a transform as it is stored (the SGLang PR #34167 page,
+section 关键源码片段: ``problem_transform`` on the output pointer; v1's
+``topk_transform_kernel``), and the DeepSeek-V4 metadata builder on the
+"[DSv4 Perf] Adaptive topk width" page (section Test/Perf) takes a
+``block_table`` and a block size.  The transform's formula is not printed;
+the reading taken is the ordinary paged-cache lookup: column ``j`` of
+request ``r`` lives in page ``block_table[r][j // page_size]`` at offset
+``j % page_size``, i.e. slot ``page * page_size + offset``; -1 stays -1.
 """
 
 from __future__ import annotations
@@ -41,6 +51,7 @@ import numpy as np
 __all__ = [
     "oracle_topk_row",
     "oracle_topk",
+    "oracle_page_slots",
     "row_view",
     "check_row",
     "is_untied",
@@ -94,6 +105,21 @@ def oracle_topk(flat: np.ndarray, row_stride: int, lengths: np.ndarray,
     for t, r in enumerate(rows):
         out[t] = oracle_topk_row(row_view(flat, row_stride, lengths[r], r), k)
     return out
+
+
+def oracle_page_slots(indices: np.ndarray, table_row: np.ndarray, page_size: int) -> np.ndarray:
+    """One output row's columns written as KV-cache slots through the page
+    table row of its request: ``table_row[j // page_size] * page_size +
+    j % page_size`` for ``j >= 0``; -1 stays -1 (see the module notes)."""
+    out = []
+    for j in np.asarray(indices).reshape(-1):
+        j = int(j)
+        if j < 0:
+            out.append(-1)
+        else:
+            page, offset = divmod(j, int(page_size))
+            out.append(int(table_row[page]) * int(page_size) + offset)
+    return np.asarray(out, dtype=np.int32)
 
 
 def _kth_largest(x: np.ndarray, m: int) -> float:

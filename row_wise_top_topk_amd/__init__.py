@@ -54,6 +54,11 @@ def load_library() -> ctypes.CDLL:
         lib.topk_indices.restype = ctypes.c_int
         lib.topk_indices_path.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, i32, i32, vp]
         lib.topk_indices_path.restype = ctypes.c_int
+        lib.topk_indices_paged.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, vp, i64, i32, vp, vp]
+        lib.topk_indices_paged.restype = ctypes.c_int
+        lib.topk_indices_paged_path.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, vp, i64, i32, vp,
+                                                i32, i32, vp]
+        lib.topk_indices_paged_path.restype = ctypes.c_int
         lib.topk_plan_describe.argtypes = [i64, i64, i32, i32, i32, ctypes.POINTER(i64)]
         lib.topk_plan_describe.restype = ctypes.c_int
         lib.topk_plan_describe_for.argtypes = [i64, i64, i32, i32, i32, i32, i32, i32, ctypes.POINTER(i64)]
@@ -119,7 +124,9 @@ def _cached_workspace(device: torch.device, stream: int, nbytes: int) -> torch.T
 
 
 def topk_indices(logits: torch.Tensor, lengths: torch.Tensor, k: int, out: torch.Tensor = None,
-                 workspace: torch.Tensor = None, path="auto", chunks: int = 0) -> torch.Tensor:
+                 workspace: torch.Tensor = None, path="auto", chunks: int = 0,
+                 block_table: torch.Tensor = None, page_size: int = 1,
+                 row_to_req: torch.Tensor = None) -> torch.Tensor:
     """Indices of the k largest of ``logits[i, :lengths[i]]`` for every row i.
 
     ``logits``: float32 device tensor, 2-D, ``stride(1) == 1``; ``stride(0)``
@@ -127,6 +134,12 @@ def topk_indices(logits: torch.Tensor, lengths: torch.Tensor, k: int, out: torch
     device tensor ``[rows]``.  Returns int32 ``[rows, k]``: selected indices in
     ascending order, then -1.  ``workspace`` (uint8, zero-filled before first
     use) is allocated and cached per stream when not given.
+
+    With ``block_table`` (int32 device tensor ``[requests, pages]``, unit
+    stride along its last axis) each selected column j of row i is written as
+    the KV-cache slot ``block_table[r, j // page_size] * page_size + j %
+    page_size``, ``r = row_to_req[i]`` (int32 ``[rows]``; default ``i``), and
+    -1 stays -1 (topk_indices_paged).
     """
     lib = load_library()
     if not isinstance(logits, torch.Tensor) or logits.dtype != torch.float32 or logits.dim() != 2:
@@ -162,10 +175,28 @@ def topk_indices(logits: torch.Tensor, lengths: torch.Tensor, k: int, out: torch
         if workspace is None:
             workspace = _cached_workspace(device, stream, need)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if block_table is None:
+        with torch.cuda.device(device):
+            st = lib.topk_indices_path(logits.data_ptr(), row_stride, lengths.data_ptr(), rows, k,
+                                       out.data_ptr(), ws_ptr, ws_bytes, pid, int(chunks), stream)
+        _check(st, "topk_indices")
+        return out
+    if (block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.device != device
+            or (block_table.shape[1] > 1 and block_table.stride(1) != 1)):
+        raise ValueError("block_table must be a 2-D int32 tensor on the logits' device with unit "
+                         "stride along its last axis")
+    req_ptr = None
+    if row_to_req is not None:
+        if (row_to_req.dtype != torch.int32 or row_to_req.dim() != 1 or row_to_req.shape[0] != rows
+                or not row_to_req.is_contiguous() or row_to_req.device != device):
+            raise ValueError("row_to_req must be a contiguous 1-D int32 tensor with one entry per row")
+        req_ptr = row_to_req.data_ptr()
     with torch.cuda.device(device):
-        st = lib.topk_indices_path(logits.data_ptr(), row_stride, lengths.data_ptr(), rows, k,
-                                   out.data_ptr(), ws_ptr, ws_bytes, pid, int(chunks), stream)
-    _check(st, "topk_indices")
+        st = lib.topk_indices_paged_path(logits.data_ptr(), row_stride, lengths.data_ptr(), rows, k,
+                                         out.data_ptr(), ws_ptr, ws_bytes, block_table.data_ptr(),
+                                         int(block_table.stride(0)), int(page_size), req_ptr, pid,
+                                         int(chunks), stream)
+    _check(st, "topk_indices_paged")
     return out
 
 

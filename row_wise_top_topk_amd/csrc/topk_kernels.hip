@@ -50,6 +50,12 @@ struct Params {
   int32_t chunk;          // split: elements per chunk, a multiple of 4
   int32_t G;              // split: workgroups per row
   int32_t rows_per_iter;  // split: rows processed per pass of the grid
+  // paged output (block_table == nullptr: the columns themselves)
+  const int32_t* block_table;  // one row of page numbers per request
+  int64_t bt_stride;           // entries between two requests' rows of block_table
+  const int32_t* row_req;      // request of each row (nullptr: row i is request i)
+  int32_t page;                // columns per page (>= 1)
+  int32_t page_log2;           // log2(page) when page is a power of two, else -1
 };
 
 // Per-row workspace of the split path.  Every field starts at zero and is
@@ -299,12 +305,29 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
 }
 
+// One output row.  Slot `at` receives column j, or -1; with a page table
+// (the index transform that follows the selection) column j of the row's
+// request is written as its KV-cache slot table[j / page] * page + j % page,
+// and -1 stays -1.
+struct OutRow {
+  int32_t* p;
+  const int32_t* table;  // the row's request's page numbers, or nullptr
+  int32_t page;
+  int32_t page_log2;
+  __device__ __forceinline__ int32_t map(int32_t j) const {
+    if (table == nullptr || j < 0) return j;
+    if (page_log2 >= 0) return (table[j >> page_log2] << page_log2) | (j & (page - 1));
+    return table[j / page] * page + j % page;
+  }
+  __device__ __forceinline__ void put(uint32_t at, int32_t j) const { p[at] = map(j); }
+};
+
 // Writes the chunk's selected elements (pred.ge) to out_row[base ...] in
 // ascending column order: a first pass counts each wavefront's selections,
 // then each position's selected lanes are placed with a ballot.
 template <int BLOCK, int E, class Pred>
 __device__ __forceinline__ void emit_regs(const uint32_t (&key)[E], const Chunk& ch,
-                                          const Pred& pred, int32_t* out_row, uint32_t base,
+                                          const Pred& pred, const OutRow& out_row, uint32_t base,
                                           uint32_t limit, uint32_t* wtot) {
   const uint32_t n = count_ge<BLOCK, E>(key, ch, pred);
   uint32_t pos_wave = base + wave_offset<BLOCK>(wave_sum(n), wtot);
@@ -315,14 +338,14 @@ __device__ __forceinline__ void emit_regs(const uint32_t (&key)[E], const Chunk&
     const bool sel = pred.ge(key[u], j);
     const uint64_t m = __ballot(sel);
     const uint32_t pos = pos_wave + lanes_below(m);
-    if (sel && pos < limit) out_row[pos] = j;
+    if (sel && pos < limit) out_row.put(pos, j);
     pos_wave += static_cast<uint32_t>(__popcll(m));
   }
 }
 
 template <int BLOCK, int E>
 __device__ __forceinline__ void emit_ordered(const uint32_t (&key)[E], const Chunk& ch,
-                                             const Prefix& p, int ib, int32_t* out_row,
+                                             const Prefix& p, int ib, const OutRow& out_row,
                                              uint32_t base, uint32_t limit, uint32_t* wtot) {
   const uint32_t rmask = (1u << ib) - 1u;
   with_pred(p, ib, rmask, [&](const auto& pred) {
@@ -330,8 +353,21 @@ __device__ __forceinline__ void emit_ordered(const uint32_t (&key)[E], const Chu
   });
 }
 
-__device__ __forceinline__ void write_trivial(int32_t* out_row, int L, int k, int nthreads) {
-  for (int t = threadIdx.x; t < k; t += nthreads) out_row[t] = t < L ? t : -1;
+__device__ __forceinline__ void write_trivial(const OutRow& out_row, int L, int k, int nthreads) {
+  for (int t = threadIdx.x; t < k; t += nthreads) out_row.put(static_cast<uint32_t>(t), t < L ? t : -1);
+}
+
+__device__ __forceinline__ OutRow out_row_of(const Params& p, int64_t row) {
+  OutRow o;
+  o.p = p.out + row * static_cast<int64_t>(p.k);
+  o.table = nullptr;
+  if (p.block_table != nullptr) {
+    const int64_t req = p.row_req != nullptr ? static_cast<int64_t>(p.row_req[row]) : row;
+    o.table = p.block_table + req * p.bt_stride;
+  }
+  o.page = p.page;
+  o.page_log2 = p.page_log2;
+  return o;
 }
 
 __device__ __forceinline__ int index_bits(int L) {
@@ -458,7 +494,7 @@ __device__ __forceinline__ uint32_t filter_wave(const uint32_t (&raw)[E], const 
 // selected columns written to out_row in ascending order.
 template <int BLOCK, int E>
 __device__ __forceinline__ void select_row(uint32_t (&raw)[E], const Chunk& ch, int L, int k,
-                                           int32_t* out_row, RowLds<BLOCK>& lds) {
+                                           const OutRow& out_row, RowLds<BLOCK>& lds) {
   constexpr int NW = BLOCK / kWave;
   const int ib = index_bits(L);
   const uint32_t rmask = (1u << ib) - 1u;
@@ -514,7 +550,7 @@ __device__ __forceinline__ void select_row(uint32_t (&raw)[E], const Chunk& ch, 
 #pragma unroll
         for (int u = 0; u < kListPerThread; ++u) {
           if (pred.ge(lst.key[u], lst.col[u])) {
-            if (pos < kk) out_row[pos] = lst.col[u];
+            if (pos < kk) out_row.put(pos, lst.col[u]);
             ++pos;
           }
         }
@@ -545,7 +581,7 @@ topk_row_kernel(Params p) {
   __shared__ RowLds<BLOCK> lds;
   const int64_t row = blockIdx.x;
   const int L = row_length(p, row);
-  int32_t* out_row = p.out + row * static_cast<int64_t>(p.k);
+  const OutRow out_row = out_row_of(p, row);
   if (L <= p.k) {
     write_trivial(out_row, L, p.k, BLOCK);
     return;
@@ -679,7 +715,7 @@ struct StreamGeom {
 // ballot per position).
 template <int BLOCK, int NP>
 __device__ __forceinline__ void select_stream_exact(const StreamGeom<BLOCK, NP>& g, int L, int k,
-                                                    int32_t* out_row, StreamLds<BLOCK>& lds) {
+                                                    const OutRow& out_row, StreamLds<BLOCK>& lds) {
   const int ib = index_bits(L);
   const uint32_t rmask = (1u << ib) - 1u;
   const uint32_t kk = static_cast<uint32_t>(k);
@@ -703,7 +739,7 @@ __device__ __forceinline__ void select_stream_exact(const StreamGeom<BLOCK, NP>&
         const bool sel = pred.ge(buf[u], j);
         const uint64_t m = __ballot(sel);
         const uint32_t pos = pos_wave + lanes_below(m);
-        if (sel && pos < kk) out_row[pos] = j;
+        if (sel && pos < kk) out_row.put(pos, j);
         pos_wave += static_cast<uint32_t>(__popcll(m));
       }
     }
@@ -773,7 +809,7 @@ topk_stream_kernel(Params p) {
   __shared__ StreamLds<BLOCK> lds;
   const int64_t row = blockIdx.x;
   const int L = row_length(p, row);
-  int32_t* out_row = p.out + row * static_cast<int64_t>(p.k);
+  const OutRow out_row = out_row_of(p, row);
   if (L <= p.k) {
     write_trivial(out_row, L, p.k, BLOCK);
     return;
@@ -905,7 +941,7 @@ topk_stream_kernel(Params p) {
 #pragma unroll
     for (int u = 0; u < kListPerThread; ++u) {
       if (pred.ge(lst.key[u], lst.col[u])) {
-        if (pos < kk) out_row[pos] = lst.col[u];
+        if (pos < kk) out_row.put(pos, lst.col[u]);
         ++pos;
       }
     }
@@ -932,7 +968,7 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* wtot) {
 
 template <int BLOCK, int E>
 __device__ __forceinline__ void select_chunk_whole_row(const uint32_t (&key)[E], const Chunk& ch,
-                                                       int L, int k, int32_t* out_row,
+                                                       int L, int k, const OutRow& out_row,
                                                        uint32_t* hist, uint32_t* wtot,
                                                        uint32_t* res) {
   const int ib = index_bits(L);
@@ -962,7 +998,7 @@ topk_split_kernel(Params p) {
     if (row >= p.num_rows) break;
     const int g = blockIdx.x % G;
     const int L = row_length(p, row);
-    int32_t* out_row = p.out + row * static_cast<int64_t>(p.k);
+    const OutRow out_row = out_row_of(p, row);
     if (L <= p.k) {
       if (g == 0) write_trivial(out_row, L, p.k, BLOCK);
       continue;
@@ -1266,7 +1302,7 @@ struct RowStream {
 // counting the ties before each entry as it goes, so ties cost no rounds
 // over index digits.
 template <int BLOCK>
-__device__ __forceinline__ void select_row_streamed(const float* row, int L, int k, int32_t* out_row,
+__device__ __forceinline__ void select_row_streamed(const float* row, int L, int k, const OutRow& out_row,
                                                  uint32_t* hist, uint32_t* wtot, uint32_t* res) {
   constexpr int NW = BLOCK / kWave;
   const RowStream<BLOCK> src(row, L);
@@ -1316,7 +1352,7 @@ __device__ __forceinline__ void select_row_streamed(const float* row, int L, int
           const bool sel = pred.ge(buf[u], j);
           const uint64_t m = __ballot(sel);
           const uint32_t at = pos + lanes_below(m);
-          if (sel && at < kk) out_row[at] = j;
+          if (sel && at < kk) out_row.put(at, j);
           pos += static_cast<uint32_t>(__popcll(m));
         }
         out_base += block_total;
@@ -1357,7 +1393,7 @@ __device__ __forceinline__ void select_row_streamed(const float* row, int L, int
       const bool sel = ((selm >> u) & 1u) != 0u;
       const uint64_t m = __ballot(sel);
       const uint32_t at = pos + lanes_below(m);
-      if (sel && at < kk) out_row[at] = e0 + u * kWave;
+      if (sel && at < kk) out_row.put(at, e0 + u * kWave);
       pos += static_cast<uint32_t>(__popcll(m));
     }
     out_base += block_total;
@@ -1381,7 +1417,7 @@ topk_chunks_kernel(Params p) {
   const int64_t row = blockIdx.x / G;
   const int g = static_cast<int>(blockIdx.x % G);
   const int L = row_length(p, row);
-  int32_t* out_row = p.out + row * static_cast<int64_t>(p.k);
+  const OutRow out_row = out_row_of(p, row);
   if (L <= p.k) {
     if (g == 0) write_trivial(out_row, L, p.k, BLOCK);
     return;
@@ -1804,12 +1840,16 @@ topk_chunks_kernel(Params p) {
           }
         }
         __syncthreads();
-        if ((reinterpret_cast<uintptr_t>(out_row) & 15u) == 0 && (kk & 3u) == 0) {
-          for (uint32_t i = 4u * static_cast<uint32_t>(tid); i < kk; i += 4u * BLOCK)
-            *reinterpret_cast<uint4*>(out_row + i) = *reinterpret_cast<const uint4*>(stage + i);
+        if ((reinterpret_cast<uintptr_t>(out_row.p) & 15u) == 0 && (kk & 3u) == 0) {
+          for (uint32_t i = 4u * static_cast<uint32_t>(tid); i < kk; i += 4u * BLOCK) {
+            const uint4 v = *reinterpret_cast<const uint4*>(stage + i);
+            *reinterpret_cast<int4*>(out_row.p + i) =
+                int4{out_row.map(static_cast<int32_t>(v.x)), out_row.map(static_cast<int32_t>(v.y)),
+                     out_row.map(static_cast<int32_t>(v.z)), out_row.map(static_cast<int32_t>(v.w))};
+          }
         } else {
           for (uint32_t i = static_cast<uint32_t>(tid); i < kk; i += BLOCK)
-            out_row[i] = static_cast<int32_t>(stage[i]);
+            out_row.put(i, static_cast<int32_t>(stage[i]));
         }
       });
     }
@@ -2035,9 +2075,18 @@ int launch(const Plan& pl, Params prm, hipStream_t stream) {
   return e == hipSuccess ? MI_TOPK_OK : MI_TOPK_ELAUNCH;
 }
 
+// Paged output: the page table, its row stride, page size and row-to-request
+// map of a topk_indices_paged call (table == nullptr: plain columns).
+struct Paging {
+  const int32_t* table = nullptr;
+  int64_t stride = 0;
+  int32_t page = 1;
+  const int32_t* row_req = nullptr;
+};
+
 int topk_impl(const float* logits, int64_t row_stride, const int32_t* lengths, int64_t num_rows,
               int32_t k, int32_t* out, void* workspace, size_t workspace_bytes, int path, int chunks,
-              hipStream_t stream) {
+              hipStream_t stream, const Paging& pg = Paging{}) {
   int st = check_shape(num_rows, row_stride, k);
   if (st != MI_TOPK_OK) return st;
   if (path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_CHUNKS || chunks < 0) return MI_TOPK_EINVAL;
@@ -2045,6 +2094,10 @@ int topk_impl(const float* logits, int64_t row_stride, const int32_t* lengths, i
   if (!logits || !lengths || !out) return MI_TOPK_EINVAL;
   if ((reinterpret_cast<uintptr_t>(logits) & 3u) || (reinterpret_cast<uintptr_t>(lengths) & 3u) ||
       (reinterpret_cast<uintptr_t>(out) & 3u))
+    return MI_TOPK_EINVAL;
+  if (pg.table != nullptr &&
+      (pg.page < 1 || pg.stride < 0 || (reinterpret_cast<uintptr_t>(pg.table) & 3u) ||
+       (reinterpret_cast<uintptr_t>(pg.row_req) & 3u)))
     return MI_TOPK_EINVAL;
   DeviceInfo dev;
   if (device_info(&dev) != hipSuccess) return MI_TOPK_ELAUNCH;
@@ -2064,6 +2117,11 @@ int topk_impl(const float* logits, int64_t row_stride, const int32_t* lengths, i
   prm.chunk = static_cast<int32_t>(pl.chunk);
   prm.G = pl.G;
   prm.rows_per_iter = pl.rows_per_iter;
+  prm.block_table = pg.table;
+  prm.bt_stride = pg.stride;
+  prm.row_req = pg.row_req;
+  prm.page = pg.page;
+  prm.page_log2 = (pg.page & (pg.page - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(pg.page)) : -1;
   return launch(pl, prm, stream);
 }
 
@@ -2095,6 +2153,32 @@ MI_TOPK_EXPORT int topk_indices_path(const float* logits, int64_t row_stride, co
                                      hipStream_t stream) {
   return topk_impl(logits, row_stride, lengths, num_rows, k, out, workspace, workspace_bytes, path,
                    chunks, stream);
+}
+
+MI_TOPK_EXPORT int topk_indices_paged_path(const float* logits, int64_t row_stride,
+                                           const int32_t* lengths, int64_t num_rows, int32_t k,
+                                           int32_t* out, void* workspace, size_t workspace_bytes,
+                                           const int32_t* block_table, int64_t block_table_stride,
+                                           int32_t page_size, const int32_t* row_to_req,
+                                           int32_t path, int32_t chunks, hipStream_t stream) {
+  if (block_table == nullptr) return MI_TOPK_EINVAL;
+  Paging pg;
+  pg.table = block_table;
+  pg.stride = block_table_stride;
+  pg.page = page_size;
+  pg.row_req = row_to_req;
+  return topk_impl(logits, row_stride, lengths, num_rows, k, out, workspace, workspace_bytes, path,
+                   chunks, stream, pg);
+}
+
+MI_TOPK_EXPORT int topk_indices_paged(const float* logits, int64_t row_stride, const int32_t* lengths,
+                                      int64_t num_rows, int32_t k, int32_t* out, void* workspace,
+                                      size_t workspace_bytes, const int32_t* block_table,
+                                      int64_t block_table_stride, int32_t page_size,
+                                      const int32_t* row_to_req, hipStream_t stream) {
+  return topk_indices_paged_path(logits, row_stride, lengths, num_rows, k, out, workspace,
+                                 workspace_bytes, block_table, block_table_stride, page_size,
+                                 row_to_req, MI_TOPK_PATH_AUTO, 0, stream);
 }
 
 namespace mitopk {

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import row_wise_top_topk_amd as mt
+from oracle import oracle_page_slots
 import workloads
 from gpu_util import SENTINEL, assert_parity, device_view, expected, run_gpu
 
@@ -243,6 +244,44 @@ def test_ties_straddle_the_threshold(stride, k, path, ties):
     ref = expected(w)
     got = run_gpu(w, path=path)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("page_size", [1, 16, 3])
+@pytest.mark.parametrize("path,stride,lengths,k,kind", [
+    ("local", 4096, [4096, 100, 1, 3000], 512, "normal"),        # register row kernel, trivial rows
+    ("local", 32768, [32768, 30000, 5, 2049], 2048, "normal"),   # streaming row kernel
+    ("chunks", 60000, [60000, 17000, 3, 40000], 1024, "bf16"),   # chunked, 16-byte output stores
+    ("chunks", 60000, [60000, 17000, 3, 40000], 1023, "normal"), # chunked, scalar output stores
+    ("chunks", 131072, [131072, 90000], 1024, "ramp"),           # chunked, streamed fallback
+    ("split", 60000, [60000, 17000, 3, 40000], 1024, "normal"),  # cooperative split
+])
+def test_paged_output(path, stride, lengths, k, kind, page_size):
+    # each selected column goes out as its KV-cache slot through the row's
+    # request's page table (rows share requests; the table's row stride
+    # exceeds its width); -1 padding stays -1
+    rows = len(lengths)
+    w = workloads.make_custom(rows, stride, lengths, k, seed=stride + k + page_size, kind=kind)
+    rng = np.random.default_rng(stride * 3 + page_size)
+    row_to_req = np.array([2, 0, 2, 1][:rows], dtype=np.int32)
+    n_req, pages = 3, -(-stride // page_size)
+    table = np.zeros((n_req, pages + 5), dtype=np.int32)
+    for r in range(n_req):
+        table[r, :pages] = rng.permutation(n_req * pages)[:pages]
+    ref = expected(w)
+    want = np.stack([oracle_page_slots(ref[i], table[row_to_req[i]], page_size) for i in range(rows)])
+    logits, lens = device_view(w)
+    got = mt.topk_indices(logits, lens, k, path=path, block_table=torch.from_numpy(table).cuda(),
+                          page_size=page_size, row_to_req=torch.from_numpy(row_to_req).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+def test_paged_output_rejects_bad_arguments():
+    w = workloads.make_custom(2, 4096, 4096, 64, seed=1)
+    logits, lens = device_view(w)
+    table = torch.zeros((2, 4096), dtype=torch.int32, device="cuda:0")
+    with pytest.raises(RuntimeError, match="status 1"):
+        mt.topk_indices(logits, lens, 64, block_table=table, page_size=0)
 
 
 def test_chunks_cluster_in_one_chunk():

@@ -13,7 +13,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import check_row, is_untied, oracle_topk, oracle_topk_row
+from oracle import check_row, is_untied, oracle_page_slots, oracle_topk, oracle_topk_row
 import oracle.topk_oracle as ot
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "strided_example.json")
@@ -212,3 +212,28 @@ def test_planted_mistakes_fail_the_pins(monkeypatch, planted):
     got = ot.oracle_topk(flat, d["row_stride"], np.array(d["lengths"]), 3, d["k"])
     failed |= got.tolist() != d["expected"]
     assert failed
+
+
+# ---- paged output: columns written as KV-cache slots through a page table
+
+def test_page_slots_hand_example():
+    # page size 4, the request's pages [7, 2, 11]: column 0 -> page 7, offset 0
+    # -> slot 28; 5 -> page 2 (second), offset 1 -> 9; 9 -> page 11, offset 1
+    # -> 45; 11 -> page 11, offset 3 -> 47; -1 stays -1
+    got = oracle_page_slots(np.array([0, 5, 9, 11, -1]), np.array([7, 2, 11]), 4)
+    assert got.tolist() == [28, 9, 45, 47, -1]
+
+
+@pytest.mark.parametrize("page_size", [1, 3, 16])
+def test_page_slots_identity_table_keeps_columns(page_size):
+    # pages numbered 0, 1, 2, ... in order: every column maps to itself
+    cols = np.array([0, 1, 2, 17, 40, 63, -1, -1])
+    table = np.arange(64)
+    assert oracle_page_slots(cols, table, page_size).tolist() == cols.tolist()
+
+
+def test_page_slots_unit_pages_are_a_lookup():
+    # one column per page: the slot is the table entry itself
+    table = np.array([50, 3, 99, 7, 12])
+    cols = np.array([4, 0, 2, -1])
+    assert oracle_page_slots(cols, table, 1).tolist() == [12, 50, 99, -1]
