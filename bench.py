@@ -10,8 +10,10 @@ HIP events on the launch stream; a separate pass with an event pair around
 each launch gives the spread of single launches.  For context the line also
 carries `read_ceiling`: a plain max (torch.amax) over the same bytes and input
 copies (rows cut into pieces when there are few), timed the same way, i.e.
-what a simple streaming read of the batch reaches on this GPU, and
-`warm_cache`: the same launches on one reused input copy.  Prints one JSON line.
+what a simple streaming read of the batch reaches on this GPU;
+`warm_cache`: the same launches on one reused input copy; and `paged_output`:
+the same launches writing KV-cache slots through a page table (the index
+transform fused into the stores).  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload prefill]
 """
@@ -125,9 +127,11 @@ def input_copies(w) -> int:
     return int(min(MAX_COPIES, max(2, -(-COLD_BYTES // footprint))))
 
 
-def time_workload(w, steps: int, warmup: int, copies: int = 2):
+def time_workload(w, steps: int, warmup: int, copies: int = 2, paging: dict | None = None):
     import row_wise_top_topk_amd as mt
     dev = torch.device("cuda:0")
+    pg = {} if paging is None else {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
+                                    for k, v in paging.items()}
     bufs = []
     for _ in range(copies):
         flat = w.flat.to(dev)
@@ -137,7 +141,7 @@ def time_workload(w, steps: int, warmup: int, copies: int = 2):
     need = mt.workspace_size(w.num_rows, w.row_stride, w.k)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev) if need else None
     for i in range(warmup):
-        mt.topk_indices(bufs[i % copies], lengths, w.k, out=out, workspace=ws)
+        mt.topk_indices(bufs[i % copies], lengths, w.k, out=out, workspace=ws, **pg)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)  # the stream the library launches on
     # per-launch event pairs, for the spread of single launches
@@ -146,7 +150,7 @@ def time_workload(w, steps: int, warmup: int, copies: int = 2):
     torch.cuda.synchronize()
     for i in range(steps):
         starts[i].record(stream)
-        mt.topk_indices(bufs[i % copies], lengths, w.k, out=out, workspace=ws)
+        mt.topk_indices(bufs[i % copies], lengths, w.k, out=out, workspace=ws, **pg)
         ends[i].record(stream)
     torch.cuda.synchronize()
     per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
@@ -157,7 +161,7 @@ def time_workload(w, steps: int, warmup: int, copies: int = 2):
     t0 = time.perf_counter()
     t_start.record(stream)
     for i in range(steps):
-        mt.topk_indices(bufs[i % copies], lengths, w.k, out=out, workspace=ws)
+        mt.topk_indices(bufs[i % copies], lengths, w.k, out=out, workspace=ws, **pg)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -166,6 +170,16 @@ def time_workload(w, steps: int, warmup: int, copies: int = 2):
     if err:
         raise RuntimeError("a cross-workgroup barrier wait gave up during the benchmark")
     return total_ms, per_launch_ms, wall
+
+
+def paging_for(w, page_size: int = 64, seed: int = 7) -> dict:
+    """Every row a token of one request whose pages are a random permutation:
+    the page table of a single long sequence in a paged KV cache."""
+    g = torch.Generator().manual_seed(seed)
+    pages = -(-w.row_stride // page_size)
+    table = torch.randperm(4 * pages, generator=g)[:pages].to(torch.int32).reshape(1, pages)
+    return {"block_table": table, "page_size": page_size,
+            "row_to_req": torch.zeros(w.num_rows, dtype=torch.int32)}
 
 
 def read_ceiling(w, steps: int, warmup: int, copies: int):
@@ -328,6 +342,12 @@ def main() -> None:
                                "rows_per_s": w2.num_rows / (t2 / args.steps * 1e-3),
                                "achieved_gbs": b2 / (m2 * 1e-3) / 1e9,
                                "frac": b2 / (m2 * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    paged_ms, _, _ = time_workload(w, args.steps, args.warmup, copies=copies, paging=paging_for(w))
+    result["paged_output"] = {"page_size": 64, "requests": 1,
+                              "launch_us_mean": paged_ms / args.steps * 1e3,
+                              "over_plain_us": (paged_ms / args.steps - avg_launch_ms) * 1e3,
+                              "note": "topk_indices_paged: columns written as KV-cache slots "
+                                      "through a random page table, fused into the stores"}
     warm_ms, _, _ = time_workload(w, args.steps, args.warmup, copies=1)
     result["warm_cache"] = {"input_copies": 1, "launch_us_mean": warm_ms / args.steps * 1e3,
                             "achieved_gbs": alg_bytes / (warm_ms / args.steps * 1e-3) / 1e9,
