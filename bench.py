@@ -63,6 +63,19 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the copy-calibrated FETCH_SIZE/WRITE_SIZE
+    counters in profiles/traffic.json, or None when the kernel sources have
+    changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    h = kernel_source_hash()
+    for t in json.load(open(TRAFFIC_FILE)):
+        if t.get("kernel_hash") == h and t.get("workload") == workload:
+            return t.get("bytes_per_launch")
+    return None
+
+
 # ---------------------------------------------------------------- CPU oracle leg
 _CPU = {}
 
@@ -293,11 +306,7 @@ def main() -> None:
     achieved = alg_bytes / (avg_launch_ms * 1e-3) / 1e9
     rows_per_s = w.num_rows / (ms_per_step * 1e-3)
 
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        t = json.load(open(TRAFFIC_FILE))
-        if t.get("kernel_hash") == kernel_source_hash() and t.get("workload") == args.workload:
-            traffic = t.get("bytes_per_launch")
+    traffic = measured_traffic(args.workload)
 
     result = {
         "metric": METRIC,
@@ -341,7 +350,12 @@ def main() -> None:
                                "launch_us_p50": float(np.percentile(pl2, 50)) * 1e3,
                                "rows_per_s": w2.num_rows / (t2 / args.steps * 1e-3),
                                "achieved_gbs": b2 / (m2 * 1e-3) / 1e9,
-                               "frac": b2 / (m2 * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                               "frac": b2 / (m2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                               "traffic": measured_traffic(args.secondary)}
+        rc2 = read_ceiling(w2, args.steps, args.warmup, c2)
+        result["secondary"]["read_ceiling"] = {"us_per_launch": rc2["us_per_launch"],
+                                               "gbs": rc2["gbs"], "frac": rc2["frac"],
+                                               "topk_over_read_time": m2 * 1e3 / rc2["us_per_launch"]}
     paged_ms, _, _ = time_workload(w, args.steps, args.warmup, copies=copies, paging=paging_for(w))
     result["paged_output"] = {"page_size": 64, "requests": 1,
                               "launch_us_mean": paged_ms / args.steps * 1e3,

@@ -4,22 +4,28 @@
 // Paths (chosen on the host from num_rows, row_stride and k; each row then
 // branches on its own length on the device):
 //   * trivial  — L_i <= k: every index 0..L_i-1, then -1.  No logits are read.
-//   * local    — one workgroup per row.  The row is read from HBM once, with
-//                16-byte loads, into registers as order-preserving keys; all
-//                radix rounds then run on-chip (LDS histograms), and the
-//                selected indices are written in ascending order.
-//   * split    — for long rows, or too few rows to fill the device: G
-//                workgroups per row each hold one chunk in registers, merge
-//                their digit histograms into a per-row workspace histogram
-//                with device-scope atomics, and meet at a per-row barrier.
-//                Once the threshold bucket is small enough its entries are
-//                gathered into a candidate list that every workgroup of the
-//                row finishes on-chip, so a row needs two barriers in the
-//                common case.  All workgroups of a launch are co-resident
-//                (cooperative launch), so the barrier waits always end.
+//   * row      — short rows (up to 8192 entries), one workgroup per row: the
+//                row in registers as order-preserving keys, radix rounds in
+//                LDS, the selected indices written in ascending order.
+//   * stream   — rows of 8K-32K entries with enough rows to fill the device,
+//                one workgroup per row: a sampled bound filters the row into
+//                an ordered LDS list while it streams in (HBM read once), and
+//                the rounds run on that list.
+//   * chunks   — long rows, or too few rows to fill the device: one
+//                workgroup per 16384-entry chunk publishes the chunk's
+//                entries above its own sampled bound; the row's last
+//                workgroup to arrive selects among them and checks that the
+//                result is exact (else streams the row itself).  Ordinary
+//                launch, no workgroup waits for another.
+//   * split    — the same shapes with k above the chunked path's limit: G
+//                workgroups per row merge digit histograms through the row
+//                workspace with device-scope atomics and meet at per-row
+//                barriers; the launch is cooperative, so every barrier wait
+//                ends.
 // The intra-row split over an 8-CTA cluster with DSMEM on the SGLang
-// PR #34167 page (TopKCluster::forward) is prior art for the split path; here
-// the merge goes through global atomics because CDNA has no clusters.
+// PR #34167 page (TopKCluster::forward) is prior art for the multi-workgroup
+// paths; here the merge goes through global memory because CDNA has no
+// clusters.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

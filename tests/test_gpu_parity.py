@@ -301,3 +301,48 @@ def test_chunks_cluster_in_one_chunk():
     for path in ("chunks", "split"):
         got = run_gpu(w, path=path)
         assert np.array_equal(got, ref), path
+
+
+def _fallback_rows(stride, k):
+    """Rows whose chunked union cannot be exact, so the last workgroup
+    selects by streaming the row: finite heads followed by -inf (the
+    threshold is -inf when fewer than k values are finite), ramps whose top
+    k sit in one chunk, plateaus and fine ramps (runs of equal values)."""
+    j = np.arange(stride, dtype=np.float64)
+    rows = []
+    rng = np.random.default_rng(stride + k)
+    for f in (0, 1, 100, k // 2, k - 1, k, k + 1, 3 * k, stride // 2):
+        x = np.full(stride, -np.inf, dtype=np.float32)
+        x[:f] = rng.standard_normal(f).astype(np.float32)
+        rows.append(x)
+    rows.append(j.astype(np.float32))                          # ascending ramp
+    rows.append((-j).astype(np.float32))                       # descending ramp
+    rows.append(np.floor(j / 100.0).astype(np.float32))        # plateaus of 100
+    rows.append(np.floor(j / 37.0).astype(np.float32))         # plateaus of 37
+    rows.append((1.0 + j * 2.0 ** -30).astype(np.float32))     # runs of 128 equal values
+    rows.append((1.0 - j * 2.0 ** -30).astype(np.float32))     # the same, descending
+    x = np.ones(stride, dtype=np.float32)
+    x[stride // 3:] = 2.0                                      # two levels, the top one tied
+    rows.append(x)
+    x = np.full(stride, 0.25, dtype=np.float32)
+    x[::1000] = 3.0                                            # sparse maxima above a constant
+    rows.append(x)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("stride,k", [(131072, 1024), (131072, 4096), (300032, 2048)])
+def test_streamed_fallback_shortcuts(stride, k):
+    # the streamed selection starts from what the chunks' union proved: a
+    # threshold fixed outright (lower bound equal to the row's largest key),
+    # a threshold equal to the lower bound (fewer than k entries above it),
+    # or a first round over the key bits below those the bounds share
+    x = _fallback_rows(stride, k)
+    rows = x.shape[0]
+    flat = torch.from_numpy(x.reshape(-1).copy())
+    lengths = torch.full((rows,), stride, dtype=torch.int32)
+    lengths[1] = stride - 5
+    w = workloads.Workload("fallback", flat, stride, lengths, rows, k)
+    ref = expected(w)
+    for path in ("auto", "chunks"):
+        got = run_gpu(w, path=path)
+        assert_parity(w, got, label=f"{path} stride {stride} k {k}")
