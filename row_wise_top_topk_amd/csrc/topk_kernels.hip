@@ -1679,8 +1679,9 @@ topk_chunks_kernel(Params p) {
   // quotient by the reciprocal ceil(2^32 / Wg) is exact for gi, Wg < 2^16.
   // The groups past G*Wg (fewer than G) all read group Wg of the last
   // chunk, at entries below kChunkCap, which hold zero whenever this union
-  // is used.  The column offsets load behind the radix rounds, which need
-  // them only for ties at the threshold.
+  // is used.  The column offsets (8 bytes per group) load right behind
+  // the keys and arrive during the radix rounds, which need them only for
+  // ties at the threshold.
   static_assert(kChunkCap == 4096, "slot = chunk << 12 | offset");
   static_assert(kUnionPerThread == 16, "four groups of four entries per thread");
   constexpr int kGroups = kUnionPerThread / 4;
@@ -1706,6 +1707,13 @@ topk_chunks_kernel(Params p) {
     sk[4 * q + 2] = v.z;
     sk[4 * q + 3] = v.w;
   }
+  // the slotted layout's column offsets go out right behind the keys (one
+  // round trip for both; waiting for the keys leaves these in flight); the
+  // packed layout loads its own instead
+  UnionList<BLOCK * E> un;
+#pragma unroll
+  for (int q = 0; q < kGroups; ++q)
+    un.offw[q] = __builtin_amdgcn_raw_buffer_load_b64(crs, gslot[q] * 2, 0, kCoherent);
   // the first window round's histogram is cleared while the keys arrive
   for (int i = tid; i < kFirstBins; i += BLOCK) hist[i] = 0;
   if (tid < kWave) {
@@ -1750,7 +1758,6 @@ topk_chunks_kernel(Params p) {
       fits && (slotted || utotal <= static_cast<uint32_t>(BLOCK * kUnionPerThread));
   bool done = false;
   if (exact_ok) {
-    UnionList<BLOCK * E> un;
     if (slotted) {
 #pragma unroll
       for (int u = 0; u < kUnionPerThread; ++u) un.sat[u] = gslot[u / 4] + static_cast<uint32_t>(u % 4);
@@ -1783,14 +1790,10 @@ topk_chunks_kernel(Params p) {
       un.key[u] = sk[u];
       nz |= sk[u];
     }
-    // the keys are consumed before the column loads go out, so no wait
-    // for those loads comes before the emission needs them
+    // the keys are consumed before the packed layout's column loads go
+    // out, so no wait for those loads comes before the emission needs them
     asm volatile("" : : "v"(nz) : "memory");
-    if (slotted) {
-#pragma unroll
-      for (int q = 0; q < kGroups; ++q)
-        un.offw[q] = __builtin_amdgcn_raw_buffer_load_b64(crs, gslot[q] * 2, 0, kCoherent);
-    } else {
+    if (!slotted) {
       uint32_t o[kUnionPerThread];
 #pragma unroll
       for (int u = 0; u < kUnionPerThread; ++u)
