@@ -1408,6 +1408,26 @@ __device__ __forceinline__ void select_row_streamed(const float* row, int L, int
   });
 }
 
+// Adds N entries per lane of a wavefront to an LDS histogram: one atomic
+// for the wavefront when every entry is taken and falls in one bin (a run of
+// equal values: constant rows, -inf tails), else one atomic per taken entry
+// (a wavefront-aggregated add per entry costs a chain of lane reads and
+// ballots; plain adds to mostly distinct bins are a few instructions).
+template <int N, class BinOf, class TakeOf>
+__device__ __forceinline__ void hist_add_entries(uint32_t* hist, BinOf bin_of, TakeOf take_of) {
+  const uint32_t b0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(bin_of(0))));
+  bool uni = true;
+#pragma unroll
+  for (int q = 0; q < N; ++q) uni = uni && take_of(q) && bin_of(q) == b0;
+  if (__ballot(!uni) == 0u) {
+    if (__lane_id() == 0) atomicAdd(&hist[b0], static_cast<uint32_t>(N * kWave));
+  } else {
+#pragma unroll
+    for (int q = 0; q < N; ++q)
+      if (take_of(q)) atomicAdd(&hist[bin_of(q)], 1u);
+  }
+}
+
 template <int BLOCK, int E>
 __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 topk_chunks_kernel(Params p) {
@@ -1490,11 +1510,9 @@ topk_chunks_kernel(Params p) {
   for (int i = tid; i < kFirstBins; i += BLOCK) hist[i] = 0;
   if (tid == 0) res[0] = 0u;
   __syncthreads();
-#pragma unroll
-  for (int q = 0; q < kChunkSamples; ++q) {
-    const uint32_t key = kv[q];
-    hist_add_wave(hist, key >> (32 - kFirstBits), key > 1u);  // kOutsideBits: key 1
-  }
+  hist_add_entries<kChunkSamples>(
+      hist, [&](int q) { return kv[q] >> (32 - kFirstBits); },
+      [&](int q) { return kv[q] > 1u; });  // positions past the row: key 1
   __syncthreads();
   find_bucket_block<BLOCK, kFirstBins>(
       hist,
@@ -1516,12 +1534,9 @@ topk_chunks_kernel(Params p) {
     __syncthreads();  // res and hist are reused
     for (int i = tid; i < kNextBins; i += BLOCK) hist[i] = 0;
     __syncthreads();
-#pragma unroll
-    for (int q = 0; q < kChunkSamples; ++q) {
-      const uint32_t key = kv[q];
-      hist_add_wave(hist, (key >> (32 - kFirstBits - kNextBits)) & (kNextBins - 1),
-                    (key >> (32 - kFirstBits)) == b0);
-    }
+    hist_add_entries<kChunkSamples>(
+        hist, [&](int q) { return (kv[q] >> (32 - kFirstBits - kNextBits)) & (kNextBins - 1); },
+        [&](int q) { return (kv[q] >> (32 - kFirstBits)) == b0; });
     __syncthreads();
     find_bucket_block<BLOCK, kNextBins>(hist, [need2](uint32_t) { return need2; }, res, wtot);
     __syncthreads();
