@@ -10,7 +10,8 @@ HIP events on the launch stream; a separate pass with an event pair around
 each launch gives the spread of single launches.  For context the line also
 carries `read_ceiling`: a plain max (torch.amax) over the same bytes and input
 copies (rows cut into pieces when there are few), timed the same way, i.e.
-what a simple streaming read of the batch reaches on this GPU;
+what a simple streaming read of the batch reaches on this GPU (also for the
+secondary workload, with the secondary's copy-calibrated HBM traffic);
 `warm_cache`: the same launches on one reused input copy; and `paged_output`:
 the same launches writing KV-cache slots through a page table (the index
 transform fused into the stores).  Prints one JSON line.
