@@ -12,9 +12,10 @@ carries `read_ceiling`: a plain max (torch.amax) over the same bytes and input
 copies (rows cut into pieces when there are few), timed the same way, i.e.
 what a simple streaming read of the batch reaches on this GPU (also for the
 secondary workload, with the secondary's copy-calibrated HBM traffic);
-`warm_cache`: the same launches on one reused input copy; and `paged_output`:
+`warm_cache`: the same launches on one reused input copy; `paged_output`:
 the same launches writing KV-cache slots through a page table (the index
-transform fused into the stores).  Prints one JSON line.
+transform fused into the stores); and `value_order`: the selection followed by
+the kernel that ranks each row's columns by value.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload prefill]
 """
@@ -141,11 +142,14 @@ def input_copies(w) -> int:
     return int(min(MAX_COPIES, max(2, -(-COLD_BYTES // footprint))))
 
 
-def time_workload(w, steps: int, warmup: int, copies: int = 2, paging: dict | None = None):
+def time_workload(w, steps: int, warmup: int, copies: int = 2, paging: dict | None = None,
+                  order: str = "column"):
     import row_wise_top_topk_amd as mt
     dev = torch.device("cuda:0")
     pg = {} if paging is None else {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
                                     for k, v in paging.items()}
+    if order != "column":
+        pg["order"] = order
     bufs = []
     for _ in range(copies):
         flat = w.flat.to(dev)
@@ -363,6 +367,11 @@ def main() -> None:
                               "over_plain_us": (paged_ms / args.steps - avg_launch_ms) * 1e3,
                               "note": "topk_indices_paged: columns written as KV-cache slots "
                                       "through a random page table, fused into the stores"}
+    vo_ms, _, _ = time_workload(w, args.steps, args.warmup, copies=copies, order="value")
+    result["value_order"] = {"launch_us_mean": vo_ms / args.steps * 1e3,
+                             "over_plain_us": (vo_ms / args.steps - avg_launch_ms) * 1e3,
+                             "note": "topk_indices(order='value'): the selection, then "
+                                     "topk_value_order ranking each row's columns by value"}
     warm_ms, _, _ = time_workload(w, args.steps, args.warmup, copies=1)
     result["warm_cache"] = {"input_copies": 1, "launch_us_mean": warm_ms / args.steps * 1e3,
                             "achieved_gbs": alg_bytes / (warm_ms / args.steps * 1e-3) / 1e9,

@@ -159,6 +159,29 @@ int topk_indices_paged_path(const float* logits, int64_t row_stride, const int32
                             hipStream_t stream);
 
 /*
+ * Value order for a selection: reorders the first m = min(k, L_i) entries of
+ * each row of `idx` (the output of topk_indices() for the same logits,
+ * row_stride, lengths and k) so that they run from the largest value to the
+ * smallest, equal values by ascending column; slots [m, k) are left as they
+ * are (-1).  The pages leave the order of the k indices open (their kernels
+ * take output slots with atomics); a caller that wants the indices ranked,
+ * as a sorted top-k returns them, asks for this order.
+ *
+ *   logits, row_stride, lengths, num_rows  as for topk_indices().
+ *   k           1 <= k <= 4096.
+ *   idx         device int32 [num_rows, k], contiguous, read and rewritten in
+ *               place; entries of [0, m) outside [0, L_i) are kept (ordered
+ *               last) and never dereferenced.
+ *   stream      HIP stream the kernel is enqueued on.
+ *
+ * One kernel launch, no workspace, no allocation.  Returns MI_TOPK_OK,
+ * MI_TOPK_EINVAL (nothing enqueued: bad sizes, k above 4096, a NULL
+ * pointer with num_rows > 0) or MI_TOPK_ELAUNCH.
+ */
+int topk_value_order(const float* logits, int64_t row_stride, const int32_t* lengths,
+                     int64_t num_rows, int32_t k, int32_t* idx, hipStream_t stream);
+
+/*
  * Describe the launch topk_indices_path() would make, without launching:
  * writes up to 7 int64 values to `info` (path, block threads, elements per
  * thread, chunk elements, chunks per row, grid workgroups, workspace bytes)

@@ -74,12 +74,14 @@ def row_view(flat: np.ndarray, row_stride: int, length: int, row: int) -> np.nda
     return flat[start:start + n]
 
 
-def oracle_topk_row(x: np.ndarray, k: int) -> np.ndarray:
+def oracle_topk_row(x: np.ndarray, k: int, order: str = "column") -> np.ndarray:
     """Top-k indices of one row's valid prefix ``x``; returns int32 of length k.
 
     A stable sort of ``-x`` orders values from largest to smallest and keeps
     equal values in index order, so its first ``m`` entries are the m largest
-    values with ties taken lowest-index first.
+    values with ties taken lowest-index first.  ``order="column"`` lists them
+    in ascending index order; ``order="value"`` keeps the sort's order (values
+    descending, equal values by ascending index), the order of a ranked top-k.
     """
     x = np.asarray(x, dtype=np.float32)
     k = int(k)
@@ -87,14 +89,18 @@ def oracle_topk_row(x: np.ndarray, k: int) -> np.ndarray:
     out = np.full(k, -1, dtype=np.int32)
     if m == 0:
         return out
-    order = np.argsort(-x, kind="stable")
-    chosen = np.sort(order[:m])
-    out[:m] = chosen.astype(np.int32)
+    ranked = np.argsort(-x, kind="stable")[:m]
+    if order == "column":
+        out[:m] = np.sort(ranked).astype(np.int32)
+    elif order == "value":
+        out[:m] = ranked.astype(np.int32)
+    else:
+        raise ValueError(f"unknown order {order!r}")
     return out
 
 
 def oracle_topk(flat: np.ndarray, row_stride: int, lengths: np.ndarray,
-                num_rows: int, k: int, rows=None) -> np.ndarray:
+                num_rows: int, k: int, rows=None, order: str = "column") -> np.ndarray:
     """Oracle for a whole batch: int32 ``[len(rows), k]`` (all rows by default)."""
     flat = np.asarray(flat, dtype=np.float32).reshape(-1)
     lengths = np.asarray(lengths).reshape(-1)
@@ -103,7 +109,7 @@ def oracle_topk(flat: np.ndarray, row_stride: int, lengths: np.ndarray,
     rows = list(rows)
     out = np.empty((len(rows), int(k)), dtype=np.int32)
     for t, r in enumerate(rows):
-        out[t] = oracle_topk_row(row_view(flat, row_stride, lengths[r], r), k)
+        out[t] = oracle_topk_row(row_view(flat, row_stride, lengths[r], r), k, order)
     return out
 
 

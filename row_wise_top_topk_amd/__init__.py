@@ -65,6 +65,8 @@ def load_library() -> ctypes.CDLL:
         lib.topk_plan_describe_for.restype = ctypes.c_int
         lib.topk_status_string.argtypes = [ctypes.c_int]
         lib.topk_status_string.restype = ctypes.c_char_p
+        lib.topk_value_order.argtypes = [vp, i64, vp, i64, i32, vp, vp]
+        lib.topk_value_order.restype = ctypes.c_int
         lib.topk_debug_keys.argtypes = [vp, vp, i64, vp]
         lib.topk_debug_keys.restype = ctypes.c_int
         _lib = lib
@@ -126,7 +128,7 @@ def _cached_workspace(device: torch.device, stream: int, nbytes: int) -> torch.T
 def topk_indices(logits: torch.Tensor, lengths: torch.Tensor, k: int, out: torch.Tensor = None,
                  workspace: torch.Tensor = None, path="auto", chunks: int = 0,
                  block_table: torch.Tensor = None, page_size: int = 1,
-                 row_to_req: torch.Tensor = None) -> torch.Tensor:
+                 row_to_req: torch.Tensor = None, order: str = "column") -> torch.Tensor:
     """Indices of the k largest of ``logits[i, :lengths[i]]`` for every row i.
 
     ``logits``: float32 device tensor, 2-D, ``stride(1) == 1``; ``stride(0)``
@@ -140,6 +142,11 @@ def topk_indices(logits: torch.Tensor, lengths: torch.Tensor, k: int, out: torch
     the KV-cache slot ``block_table[r, j // page_size] * page_size + j %
     page_size``, ``r = row_to_req[i]`` (int32 ``[rows]``; default ``i``), and
     -1 stays -1 (topk_indices_paged).
+
+    ``order="value"`` returns each row's selected columns from the largest
+    value to the smallest (equal values by ascending column) instead of in
+    ascending column order (topk_value_order after the selection; k <= 4096,
+    not with a page table).
     """
     lib = load_library()
     if not isinstance(logits, torch.Tensor) or logits.dtype != torch.float32 or logits.dim() != 2:
@@ -165,6 +172,10 @@ def topk_indices(logits: torch.Tensor, lengths: torch.Tensor, k: int, out: torch
     elif (out.dtype != torch.int32 or tuple(out.shape) != (rows, k) or not out.is_contiguous()
           or out.device != device):
         raise ValueError("out must be a contiguous int32 [rows, k] tensor on the logits' device")
+    if order not in ("column", "value"):
+        raise ValueError("order must be 'column' or 'value'")
+    if order == "value" and (k > 4096 or block_table is not None):
+        raise ValueError("order='value' takes k <= 4096 and no page table")
     if rows == 0:
         return out
     pid = _path_id(path)
@@ -180,6 +191,11 @@ def topk_indices(logits: torch.Tensor, lengths: torch.Tensor, k: int, out: torch
             st = lib.topk_indices_path(logits.data_ptr(), row_stride, lengths.data_ptr(), rows, k,
                                        out.data_ptr(), ws_ptr, ws_bytes, pid, int(chunks), stream)
         _check(st, "topk_indices")
+        if order == "value":
+            with torch.cuda.device(device):
+                st = lib.topk_value_order(logits.data_ptr(), row_stride, lengths.data_ptr(), rows, k,
+                                          out.data_ptr(), stream)
+            _check(st, "topk_value_order")
         return out
     if (block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.device != device
             or (block_table.shape[1] > 1 and block_table.stride(1) != 1)):

@@ -1920,6 +1920,60 @@ __global__ void debug_keys_kernel(const float* in, uint32_t* out, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------
+// Value order: the selected columns of a row reordered by value (largest
+// first, equal values by ascending column).  One workgroup per row gathers
+// the m = min(k, L_i) selected values, forms the composite (key : reversed
+// column), whose descending order is the wanted one, and sorts the
+// composites of the row in LDS with a bitonic network; slots [m, k) keep -1.
+// ---------------------------------------------------------------------------
+constexpr int kSortMaxK = 4096;  // composites per row held in LDS (32 KB)
+
+template <int BLOCK>
+__global__ void __launch_bounds__(BLOCK) topk_value_order_kernel(const float* logits, int64_t row_stride,
+                                                              const int32_t* lengths, int32_t k,
+                                                              int32_t* idx) {
+  __shared__ uint64_t comp[kSortMaxK];
+  const int64_t row = blockIdx.x;
+  int64_t L = lengths[row];
+  L = L < 0 ? 0 : (L > row_stride ? row_stride : L);
+  const int m = static_cast<int>(L < k ? L : k);
+  if (m <= 1) return;
+  int n = 1;
+  while (n < m) n <<= 1;  // sorted size (power of two, at most kSortMaxK)
+  const float* row_ptr = logits + row * row_stride;
+  int32_t* out = idx + row * static_cast<int64_t>(k);
+  for (int i = threadIdx.x; i < n; i += BLOCK) {
+    uint64_t c = 0;  // padding sorts after every entry
+    if (i < m) {
+      const int32_t j = out[i];
+      // a column outside the row (not a selection's output) reads nothing
+      const bool ok = j >= 0 && j < L;
+      const uint32_t key = ok ? order_key(row_ptr[j]) : 0u;
+      c = (static_cast<uint64_t>(key) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(j));
+    }
+    comp[i] = c;
+  }
+  __syncthreads();
+  // bitonic network, descending: pairs (i, i + s) with bit s of i clear
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int s = size >> 1; s > 0; s >>= 1) {
+      for (int t = threadIdx.x; t < (n >> 1); t += BLOCK) {
+        const int i = ((t & ~(s - 1)) << 1) | (t & (s - 1));
+        const uint64_t a = comp[i], b = comp[i + s];
+        const bool first_desc = (i & size) == 0;  // this block of the network runs descending
+        if (first_desc ? a < b : a > b) {
+          comp[i] = b;
+          comp[i + s] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < m; i += BLOCK)
+    out[i] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(comp[i]));
+}
+
+// ---------------------------------------------------------------------------
 // Host side: planning and launch.
 // ---------------------------------------------------------------------------
 enum Kind { kRow256x16, kRow512x16, kSplit512x32, kStream512x32, kStream512x64, kChunks512x32,
@@ -2262,6 +2316,17 @@ MI_TOPK_EXPORT const char* topk_status_string(int status) {
     case MI_TOPK_ETOOLONG: return "rows too long for the device";
     default: return "unknown status";
   }
+}
+
+MI_TOPK_EXPORT int topk_value_order(const float* logits, int64_t row_stride, const int32_t* lengths,
+                                    int64_t num_rows, int32_t k, int32_t* idx, hipStream_t stream) {
+  if (num_rows < 0 || num_rows > INT32_MAX || row_stride < 1 || k < 1 || k > kSortMaxK)
+    return MI_TOPK_EINVAL;
+  if (num_rows == 0) return MI_TOPK_OK;
+  if (!logits || !lengths || !idx) return MI_TOPK_EINVAL;
+  hipLaunchKernelGGL(topk_value_order_kernel<512>, dim3(static_cast<unsigned>(num_rows)), dim3(512), 0, stream,
+                     logits, row_stride, lengths, k, idx);
+  return hipGetLastError() == hipSuccess ? MI_TOPK_OK : MI_TOPK_ELAUNCH;
 }
 
 MI_TOPK_EXPORT int topk_debug_keys(const float* in, uint32_t* out, int64_t n, hipStream_t stream) {

@@ -74,3 +74,11 @@ def test_invalid_arguments_rejected_before_any_device_call(lib):
     assert lib.topk_workspace_size(-1, 8, 4) == 0
     assert lib.topk_workspace_size(3, 8, 0) == 0
     assert lib.topk_debug_keys(None, None, -1, None) == 1
+    vo = lib.topk_value_order
+    assert vo(fake, 8, fake, 3, 4097, fake, None) == 1                   # k above 4096
+    assert vo(fake, 8, fake, 3, 0, fake, None) == 1                      # k == 0
+    assert vo(fake, 0, fake, 3, 4, fake, None) == 1                      # row_stride < 1
+    assert vo(fake, 8, fake, -1, 4, fake, None) == 1                     # num_rows < 0
+    assert vo(None, 8, fake, 3, 4, fake, None) == 1                      # NULL logits
+    assert vo(fake, 8, fake, 3, 4, None, None) == 1                      # NULL idx
+    assert vo(fake, 8, fake, 0, 4, fake, None) == 0                      # empty batch: no-op

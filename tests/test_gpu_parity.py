@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import row_wise_top_topk_amd as mt
-from oracle import oracle_page_slots
+from oracle import oracle_page_slots, oracle_topk
 import workloads
 from gpu_util import SENTINEL, assert_parity, device_view, expected, run_gpu
 
@@ -346,3 +346,40 @@ def test_streamed_fallback_shortcuts(stride, k):
     for path in ("auto", "chunks"):
         got = run_gpu(w, path=path)
         assert_parity(w, got, label=f"{path} stride {stride} k {k}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "long", "prefill", "adversarial"])
+def test_value_order_named_workloads(name):
+    # the selected columns ranked by value (descending, ties by column), on
+    # the kernel each batch shape takes
+    w = workloads.make(name)
+    logits, lengths = device_view(w)
+    out = torch.full((w.num_rows, w.k), SENTINEL, dtype=torch.int32, device="cuda:0")
+    mt.topk_indices(logits, lengths, w.k, out=out, order="value")
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    exp = oracle_topk(w.flat.numpy(), w.row_stride, w.lengths.numpy(), w.num_rows, w.k, order="value")
+    bad = np.nonzero(np.any(got != exp, axis=1))[0]
+    assert bad.size == 0, f"{name}: {bad.size} rows differ, first {int(bad[0])}"
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 64, 65, 1000, 4096])
+@pytest.mark.parametrize("kind", ["normal", "bf16", "levels", "equal"])
+def test_value_order_k_and_ties(k, kind):
+    stride = 6007  # odd stride, ragged lengths, some rows shorter than k
+    lengths = [6007, 5000, 4097, 4096, 100, 1, 0, 3000]
+    w = workloads.make_custom(len(lengths), stride, lengths, k, seed=90 + k, kind=kind)
+    logits, lens = device_view(w, offset=1)
+    out = mt.topk_indices(logits, lens, k, order="value")
+    torch.cuda.synchronize()
+    exp = oracle_topk(w.flat.numpy(), stride, w.lengths.numpy(), w.num_rows, k, order="value")
+    assert np.array_equal(out.cpu().numpy(), exp)
+
+
+def test_value_order_rejects_bad_arguments():
+    w = workloads.make_custom(2, 8192, [8192, 100], 4097, seed=5)
+    logits, lens = device_view(w)
+    with pytest.raises(ValueError):
+        mt.topk_indices(logits, lens, 4097, order="value")
+    with pytest.raises(ValueError):
+        mt.topk_indices(logits, lens, 16, order="random")

@@ -186,7 +186,7 @@ def test_checker_flags_mutations():
     assert check_row(x[:10], k, short[:-1])         # wrong slot count
 
 
-def _planted_highest_index_ties(x, k):
+def _planted_highest_index_ties(x, k, order="column"):
     """A plausible mistake: reversing an ascending sort (highest index on ties)."""
     x = np.asarray(x, dtype=np.float32)
     m = min(k, x.shape[0])
@@ -195,7 +195,7 @@ def _planted_highest_index_ties(x, k):
     return out
 
 
-def _planted_no_padding(x, k):
+def _planted_no_padding(x, k, order="column"):
     """A plausible mistake: short rows not padded with -1."""
     x = np.asarray(x, dtype=np.float32)
     m = min(k, x.shape[0])
@@ -237,3 +237,50 @@ def test_page_slots_unit_pages_are_a_lookup():
     table = np.array([50, 3, 99, 7, 12])
     cols = np.array([4, 0, 2, -1])
     assert oracle_page_slots(cols, table, 1).tolist() == [12, 50, 99, -1]
+
+
+# ---- value order: the selected columns ranked by value
+
+def _ranked_by_definition(x, k):
+    """Brute force: every index sorted by (value descending, index ascending)
+    with Python's own sort, cut to m, then -1."""
+    x = [float(v) for v in x]
+    m = min(k, len(x))
+    ranked = sorted(range(len(x)), key=lambda j: (-x[j], j))[:m]
+    return ranked + [-1] * (k - m)
+
+
+def test_value_order_hand_examples():
+    # 7.0 (column 4), then the two 2.0 values in column order, then 0.5 and -0.0
+    x = [0.5, -1.0, 2.0, 2.0, 7.0, -0.0]
+    assert ot.oracle_topk_row(np.array(x, dtype=np.float32), 3, "value").tolist() == [4, 2, 3]
+    assert ot.oracle_topk_row(np.array(x, dtype=np.float32), 5, "value").tolist() == [4, 2, 3, 0, 5]
+    # +0.0 and -0.0 are equal values: the lower column first
+    assert ot.oracle_topk_row(np.array([0.0, -0.0, -1.0], dtype=np.float32), 2, "value").tolist() == [0, 1]
+    assert ot.oracle_topk_row(np.array([-0.0, 0.0, -1.0], dtype=np.float32), 2, "value").tolist() == [0, 1]
+    # -inf is a value; a short row is padded
+    assert ot.oracle_topk_row(np.array([-np.inf, 1.0], dtype=np.float32), 4, "value").tolist() == [1, 0, -1, -1]
+
+
+def test_value_order_matches_brute_force_and_the_column_set():
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        L = int(rng.integers(0, 12))
+        k = int(rng.integers(1, 14))
+        x = rng.integers(-3, 4, size=L).astype(np.float32)  # many ties
+        got = ot.oracle_topk_row(x, k, "value")
+        assert got.tolist() == _ranked_by_definition(x, k)
+        col = ot.oracle_topk_row(x, k, "column")
+        assert sorted(got.tolist()) == sorted(col.tolist())
+        m = min(k, L)
+        vals = x[got[:m]]
+        assert np.all(vals[:-1] >= vals[1:])
+
+
+def test_value_order_batch_uses_the_row_layout():
+    d, flat = _load_golden()
+    got = ot.oracle_topk(flat, d["row_stride"], np.array(d["lengths"]), 3, d["k"], order="value")
+    col = ot.oracle_topk(flat, d["row_stride"], np.array(d["lengths"]), 3, d["k"])
+    assert [sorted(r) for r in got.tolist()] == [sorted(r) for r in col.tolist()]
+    with pytest.raises(ValueError):
+        ot.oracle_topk_row(np.zeros(3, dtype=np.float32), 2, "random")
