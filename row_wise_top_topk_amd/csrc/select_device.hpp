@@ -392,7 +392,7 @@ __device__ __forceinline__ Prefix rounds_local(const Src& src, Prefix p, uint32_
 // The last step when the bucket of key prefix kp (the top 32 - sh key bits)
 // holds at most 64 entries: they are gathered into LDS (lds[2i] key,
 // lds[2i + 1] column, in any order; res[3] counts them and must be zero on
-// entry), and one wavefront ranks each against the others by the composite
+// entry), and the wavefronts rank them against each other by the composite
 // (key, then lower column first); the entry of rank need - 1 is the last one
 // selected.  Returns the prefix that selects exactly the need entries of the
 // bucket: key >= T (32 bits) when no entry with key T falls below it, else
@@ -408,26 +408,29 @@ __device__ __forceinline__ Prefix finish_small(const Src& src, uint32_t kp, int 
     }
   });
   __syncthreads();
-  if (threadIdx.x < kWave) {
+  {
+    // Every wavefront holds the n entries on its lanes (lane l: entry l) and
+    // ranks entries i = w, w + NW, ...: the rank of entry i is the number of
+    // entries ordered before it, one ballot.  The wavefront holding rank
+    // need - 1 (there is exactly one) reports it.
     const uint32_t n = res[3];
     const uint32_t lane = __lane_id();
-    const uint32_t k = lane < n ? lds[2 * lane] : 0u;
-    const uint32_t j = lane < n ? lds[2 * lane + 1] : 0u;
-    uint32_t rank = 0;  // entries of the bucket ordered before this one
-    for (uint32_t i = 0; i < n; ++i) {
-      const uint32_t ki = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(k), static_cast<int>(i)));
-      const uint32_t ji = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(j), static_cast<int>(i)));
-      rank += (ki > k || (ki == k && ji < j)) ? 1u : 0u;
-    }
-    const uint64_t m = __ballot(lane < n && rank == need - 1u);
-    const int tl = __ffsll(static_cast<unsigned long long>(m)) - 1;
-    const uint32_t T = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(k), tl));
-    const uint32_t jt = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(j), tl));
-    const uint64_t tie_below = __ballot(lane < n && k == T && rank >= need);
-    if (lane == 0) {
-      res[0] = T;
-      res[1] = jt;
-      res[2] = tie_below != 0 ? 1u : 0u;
+    const uint32_t kl = lane < n ? lds[2 * lane] : 0u;
+    const uint32_t jl = lane < n ? lds[2 * lane + 1] : 0u;
+    constexpr uint32_t nw = BLOCK / kWave;
+    const uint32_t w = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave)));
+    for (uint32_t i = w; i < n; i += nw) {
+      const uint32_t ki = lds[2 * i], ji = lds[2 * i + 1];
+      const uint64_t before = __ballot(lane < n && (kl > ki || (kl == ki && jl < ji)));
+      if (static_cast<uint32_t>(__popcll(before)) == need - 1u) {
+        // an entry with key T ordered after (T, jt) is left out
+        const uint64_t tie_below = __ballot(lane < n && kl == ki && jl > ji);
+        if (lane == 0) {
+          res[0] = ki;
+          res[1] = ji;
+          res[2] = tie_below != 0 ? 1u : 0u;
+        }
+      }
     }
   }
   __syncthreads();
