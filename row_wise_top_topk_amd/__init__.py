@@ -25,7 +25,7 @@ _PATHS = {"auto": PATH_AUTO, "local": PATH_LOCAL, "split": PATH_SPLIT, "chunks":
 MAX_K = 1 << 24
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_lib = None
+_libs: dict = {}
 _lib_lock = threading.Lock()
 _ws_cache: dict = {}
 
@@ -34,42 +34,49 @@ def library_path() -> str:
     return os.environ.get("MI_TOPK_LIB", os.path.join(_HERE, "libmi_topk.so"))
 
 
-def load_library() -> ctypes.CDLL:
-    """Load libmi_topk.so once; raise if it is missing."""
-    global _lib
+def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Argument and result types of every exported function."""
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    lib.topk_workspace_size.argtypes = [i64, i64, i32]
+    lib.topk_workspace_size.restype = sz
+    lib.topk_workspace_size_path.argtypes = [i64, i64, i32, i32, i32]
+    lib.topk_workspace_size_path.restype = sz
+    lib.topk_indices.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, vp]
+    lib.topk_indices.restype = ctypes.c_int
+    lib.topk_indices_path.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, i32, i32, vp]
+    lib.topk_indices_path.restype = ctypes.c_int
+    lib.topk_indices_paged.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, vp, i64, i32, vp, vp]
+    lib.topk_indices_paged.restype = ctypes.c_int
+    lib.topk_indices_paged_path.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, vp, i64, i32, vp,
+                                            i32, i32, vp]
+    lib.topk_indices_paged_path.restype = ctypes.c_int
+    lib.topk_plan_describe.argtypes = [i64, i64, i32, i32, i32, ctypes.POINTER(i64)]
+    lib.topk_plan_describe.restype = ctypes.c_int
+    lib.topk_plan_describe_for.argtypes = [i64, i64, i32, i32, i32, i32, i32, i32, ctypes.POINTER(i64)]
+    lib.topk_plan_describe_for.restype = ctypes.c_int
+    lib.topk_status_string.argtypes = [ctypes.c_int]
+    lib.topk_status_string.restype = ctypes.c_char_p
+    lib.topk_value_order.argtypes = [vp, i64, vp, i64, i32, vp, vp]
+    lib.topk_value_order.restype = ctypes.c_int
+    lib.topk_debug_keys.argtypes = [vp, vp, i64, vp]
+    lib.topk_debug_keys.restype = ctypes.c_int
+    return lib
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load a build of the library once (default: ``library_path()``); raise
+    if it is missing.  Other paths (e.g. a build at another optimisation
+    level) are loaded side by side."""
+    path = library_path() if path is None else os.path.abspath(path)
     with _lib_lock:
-        if _lib is not None:
-            return _lib
-        path = library_path()
+        lib = _libs.get(path)
+        if lib is not None:
+            return lib
         if not os.path.exists(path):
             raise RuntimeError(
                 f"{path} is missing: build it with `python -m row_wise_top_topk_amd.build`")
-        lib = ctypes.CDLL(path)
-        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
-        lib.topk_workspace_size.argtypes = [i64, i64, i32]
-        lib.topk_workspace_size.restype = sz
-        lib.topk_workspace_size_path.argtypes = [i64, i64, i32, i32, i32]
-        lib.topk_workspace_size_path.restype = sz
-        lib.topk_indices.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, vp]
-        lib.topk_indices.restype = ctypes.c_int
-        lib.topk_indices_path.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, i32, i32, vp]
-        lib.topk_indices_path.restype = ctypes.c_int
-        lib.topk_indices_paged.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, vp, i64, i32, vp, vp]
-        lib.topk_indices_paged.restype = ctypes.c_int
-        lib.topk_indices_paged_path.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, vp, i64, i32, vp,
-                                                i32, i32, vp]
-        lib.topk_indices_paged_path.restype = ctypes.c_int
-        lib.topk_plan_describe.argtypes = [i64, i64, i32, i32, i32, ctypes.POINTER(i64)]
-        lib.topk_plan_describe.restype = ctypes.c_int
-        lib.topk_plan_describe_for.argtypes = [i64, i64, i32, i32, i32, i32, i32, i32, ctypes.POINTER(i64)]
-        lib.topk_plan_describe_for.restype = ctypes.c_int
-        lib.topk_status_string.argtypes = [ctypes.c_int]
-        lib.topk_status_string.restype = ctypes.c_char_p
-        lib.topk_value_order.argtypes = [vp, i64, vp, i64, i32, vp, vp]
-        lib.topk_value_order.restype = ctypes.c_int
-        lib.topk_debug_keys.argtypes = [vp, vp, i64, vp]
-        lib.topk_debug_keys.restype = ctypes.c_int
-        _lib = lib
+        lib = _declare(ctypes.CDLL(path))
+        _libs[path] = lib
         return lib
 
 
@@ -120,6 +127,11 @@ def _cached_workspace(device: torch.device, stream: int, nbytes: int) -> torch.T
     key = (device.index, stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(
+                "topk_indices needs a workspace for this shape and is called under stream "
+                "capture, where it allocates nothing: pass workspace= (zero-filled, "
+                "workspace_size() bytes) allocated before the capture")
         ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
@@ -128,14 +140,27 @@ def _cached_workspace(device: torch.device, stream: int, nbytes: int) -> torch.T
 def topk_indices(logits: torch.Tensor, lengths: torch.Tensor, k: int, out: torch.Tensor = None,
                  workspace: torch.Tensor = None, path="auto", chunks: int = 0,
                  block_table: torch.Tensor = None, page_size: int = 1,
-                 row_to_req: torch.Tensor = None, order: str = "column") -> torch.Tensor:
-    """Indices of the k largest of ``logits[i, :lengths[i]]`` for every row i.
+                 row_to_req: torch.Tensor = None, order: str = "column",
+                 library: str | None = None, check_workspace: bool = False) -> torch.Tensor:
+    """Indices of the k largest of ``logits[i, :L_i]`` for every row i, where
+    ``L_i = lengths[i]`` clamped into ``[0, logits.stride(0)]``.
 
     ``logits``: float32 device tensor, 2-D, ``stride(1) == 1``; ``stride(0)``
-    is passed as the row stride (it may exceed the width).  ``lengths``: int32
-    device tensor ``[rows]``.  Returns int32 ``[rows, k]``: selected indices in
-    ascending order, then -1.  ``workspace`` (uint8, zero-filled before first
-    use) is allocated and cached per stream when not given.
+    is passed as the row stride (it may exceed the width: a view sliced from
+    a padded buffer).  ``lengths``: int32 device tensor ``[rows]``.  Lengths
+    are clamped to the row stride, not to ``logits.shape[1]``: entries between
+    the width and the stride of a sliced view are read when a length exceeds
+    the width, so keep ``lengths <= logits.shape[1]`` unless that memory is
+    yours (on the last row it may lie past the tensor's storage).  Returns
+    int32 ``[rows, k]``: selected indices in ascending order, then -1.
+
+    ``workspace`` (uint8, zero-filled before its first use, at least
+    ``workspace_size()`` bytes) is allocated and cached per stream when not
+    given; under stream capture nothing is allocated, and a call that needs a
+    workspace and has none raises.  The workspace's first word is a sticky
+    error flag (a cross-workgroup wait of the cooperative split path gave up);
+    ``check_workspace=True`` reads it after the call (a synchronisation), and
+    on a set flag zero-fills the workspace and raises.
 
     With ``block_table`` (int32 device tensor ``[requests, pages]``, unit
     stride along its last axis) each selected column j of row i is written as
@@ -145,10 +170,12 @@ def topk_indices(logits: torch.Tensor, lengths: torch.Tensor, k: int, out: torch
 
     ``order="value"`` returns each row's selected columns from the largest
     value to the smallest (equal values by ascending column) instead of in
-    ascending column order (topk_value_order after the selection; k <= 4096,
-    not with a page table).
+    ascending column order (k <= 4096, not with a page table).
+
+    ``library``: path of another build of the library to call (default: the
+    in-tree ``libmi_topk.so``).
     """
-    lib = load_library()
+    lib = load_library(library)
     if not isinstance(logits, torch.Tensor) or logits.dtype != torch.float32 or logits.dim() != 2:
         raise ValueError("logits must be a 2-D float32 tensor")
     if not logits.is_cuda:
@@ -196,23 +223,27 @@ def topk_indices(logits: torch.Tensor, lengths: torch.Tensor, k: int, out: torch
                 st = lib.topk_value_order(logits.data_ptr(), row_stride, lengths.data_ptr(), rows, k,
                                           out.data_ptr(), stream)
             _check(st, "topk_value_order")
-        return out
-    if (block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.device != device
-            or (block_table.shape[1] > 1 and block_table.stride(1) != 1)):
-        raise ValueError("block_table must be a 2-D int32 tensor on the logits' device with unit "
-                         "stride along its last axis")
-    req_ptr = None
-    if row_to_req is not None:
-        if (row_to_req.dtype != torch.int32 or row_to_req.dim() != 1 or row_to_req.shape[0] != rows
-                or not row_to_req.is_contiguous() or row_to_req.device != device):
-            raise ValueError("row_to_req must be a contiguous 1-D int32 tensor with one entry per row")
-        req_ptr = row_to_req.data_ptr()
-    with torch.cuda.device(device):
-        st = lib.topk_indices_paged_path(logits.data_ptr(), row_stride, lengths.data_ptr(), rows, k,
-                                         out.data_ptr(), ws_ptr, ws_bytes, block_table.data_ptr(),
-                                         int(block_table.stride(0)), int(page_size), req_ptr, pid,
-                                         int(chunks), stream)
-    _check(st, "topk_indices_paged")
+    else:
+        if (block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.device != device
+                or (block_table.shape[1] > 1 and block_table.stride(1) != 1)):
+            raise ValueError("block_table must be a 2-D int32 tensor on the logits' device with unit "
+                             "stride along its last axis")
+        req_ptr = None
+        if row_to_req is not None:
+            if (row_to_req.dtype != torch.int32 or row_to_req.dim() != 1 or row_to_req.shape[0] != rows
+                    or not row_to_req.is_contiguous() or row_to_req.device != device):
+                raise ValueError("row_to_req must be a contiguous 1-D int32 tensor with one entry per row")
+            req_ptr = row_to_req.data_ptr()
+        with torch.cuda.device(device):
+            st = lib.topk_indices_paged_path(logits.data_ptr(), row_stride, lengths.data_ptr(), rows, k,
+                                             out.data_ptr(), ws_ptr, ws_bytes, block_table.data_ptr(),
+                                             int(block_table.stride(0)), int(page_size), req_ptr, pid,
+                                             int(chunks), stream)
+        _check(st, "topk_indices_paged")
+    if check_workspace and workspace is not None and need > 0 and workspace_error(workspace):
+        workspace.zero_()
+        raise RuntimeError("a cross-workgroup wait of the split path gave up: this call's output "
+                           "is invalid (the workspace has been zero-filled again)")
     return out
 
 
