@@ -57,6 +57,7 @@ extern "C" {
 #define MI_TOPK_EWORKSPACE 2 /* workspace_bytes below topk_workspace_size()       */
 #define MI_TOPK_ELAUNCH 3    /* a HIP call failed (launch or device query)         */
 #define MI_TOPK_ETOOLONG 4   /* rows too long to keep on chip across the device    */
+#define MI_TOPK_ESCRATCH 5   /* batch needs more than MI_TOPK_NOALLOC_WORKSPACE    */
 
 /* Largest k accepted. */
 #define MI_TOPK_MAX_K (1 << 24)
@@ -201,6 +202,28 @@ int topk_plan_describe(int64_t num_rows, int64_t row_stride, int32_t k, int32_t 
 int topk_plan_describe_for(int64_t num_rows, int64_t row_stride, int32_t k, int32_t path,
                            int32_t chunks, int32_t cus, int32_t coop, int32_t split_per_cu,
                            int64_t* info);
+
+/*
+ * topk_indices() for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and result as topk_indices() without the workspace pair:
+ * the workspace is a fixed array of MI_TOPK_NOALLOC_WORKSPACE bytes that the
+ * library holds on every device it runs on until the process ends.  The call
+ * allocates nothing and frees nothing.  On the first call on a device the
+ * array's address is looked up and the array is zero-filled (a kernel on
+ * `stream`; make that first call outside graph capture, or the fill becomes
+ * part of the graph).  Every call on a device shares that device's array:
+ * calls that may overlap in time on one device (different streams, or
+ * threads without ordering) race and give wrong results; calls ordered on
+ * one stream are fine.  Returns MI_TOPK_ESCRATCH, with nothing enqueued,
+ * when the batch needs more workspace than the array holds (one 900K-entry
+ * row of the chunked path needs about 1.35 MB; topk_workspace_size() gives
+ * the need), else as topk_indices().
+ */
+#define MI_TOPK_NOALLOC_WORKSPACE ((size_t)64 << 20)
+
+int topk_indices_noalloc(const float* logits, int64_t row_stride, const int32_t* lengths,
+                         int64_t num_rows, int32_t k, int32_t* out, hipStream_t stream);
 
 /*
  * Diagnostic: the order-preserving key the kernels give each fp32 value

@@ -60,6 +60,8 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.topk_value_order.restype = ctypes.c_int
     lib.topk_debug_keys.argtypes = [vp, vp, i64, vp]
     lib.topk_debug_keys.restype = ctypes.c_int
+    lib.topk_indices_noalloc.argtypes = [vp, i64, vp, i64, i32, vp, vp]
+    lib.topk_indices_noalloc.restype = ctypes.c_int
     return lib
 
 

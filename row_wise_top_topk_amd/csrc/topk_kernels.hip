@@ -1919,6 +1919,14 @@ __global__ void debug_keys_kernel(const float* in, uint32_t* out, int64_t n) {
   if (i < n) out[i] = order_key(in[i]);
 }
 
+// Zero-fills n 16-byte words with vector stores (a kernel rather than a
+// memset, so that a call captured in a graph records a kernel node).
+__global__ void __launch_bounds__(256) fill_zero_kernel(uint4* p, int64_t n) {
+  const int64_t step = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += step)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 // ---------------------------------------------------------------------------
 // Value order: the selected columns of a row reordered by value (largest
 // first, equal values by ascending column).  One workgroup per row gathers
@@ -2314,6 +2322,7 @@ MI_TOPK_EXPORT const char* topk_status_string(int status) {
     case MI_TOPK_EWORKSPACE: return "workspace too small";
     case MI_TOPK_ELAUNCH: return "HIP launch or device query failed";
     case MI_TOPK_ETOOLONG: return "rows too long for the device";
+    case MI_TOPK_ESCRATCH: return "batch needs more workspace than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }
@@ -2337,4 +2346,91 @@ MI_TOPK_EXPORT int topk_debug_keys(const float* in, uint32_t* out, int64_t n, hi
   if (blocks > INT32_MAX) return MI_TOPK_EINVAL;
   hipLaunchKernelGGL(debug_keys_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, in, out, n);
   return hipGetLastError() == hipSuccess ? MI_TOPK_OK : MI_TOPK_ELAUNCH;
+}
+
+// ---------------------------------------------------------------------------
+// The no-allocation entry point: topk_indices() with its workspace in a
+// fixed device array instead of a caller's buffer.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = MI_TOPK_NOALLOC_WORKSPACE;
+}  // namespace
+
+// One copy per device, held until the process ends.  In host code this name
+// stands for the array but is not its device address: the address is taken
+// once per device with hipGetSymbolAddress (scratch_of below) and only that
+// pointer is ever passed to a kernel.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+namespace mitopk {
+namespace {
+
+std::once_flag g_scratch_once[kMaxDevices];
+uint8_t* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_status[kMaxDevices];
+std::once_flag g_scratch_clear_once[kMaxDevices];
+hipError_t g_scratch_clear_status[kMaxDevices];
+
+int fill_zero(uint8_t* p, size_t bytes, hipStream_t stream) {
+  const int64_t n = static_cast<int64_t>((bytes + 15) / 16);
+  if (n == 0) return MI_TOPK_OK;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     reinterpret_cast<uint4*>(p), n);
+  return hipGetLastError() == hipSuccess ? MI_TOPK_OK : MI_TOPK_ELAUNCH;
+}
+
+// The current device's scratch address, taken on the first call on that
+// device (with it current), and the scratch zero-filled on the stream of
+// that first call (the kernels need it zero before their first use and
+// leave it zero after every call).
+int scratch_of(hipStream_t stream, uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MI_TOPK_ELAUNCH;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* ptr = nullptr;
+    g_scratch_status[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(ptr);
+  });
+  if (g_scratch_status[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return MI_TOPK_ELAUNCH;
+  std::call_once(g_scratch_clear_once[dev], [dev, stream]() {
+    g_scratch_clear_status[dev] =
+        fill_zero(g_scratch_ptr[dev], kScratchBytes, stream) == MI_TOPK_OK ? hipSuccess : hipErrorLaunchFailure;
+  });
+  if (g_scratch_clear_status[dev] != hipSuccess) return MI_TOPK_ELAUNCH;
+  *out = g_scratch_ptr[dev];
+  return MI_TOPK_OK;
+}
+
+}  // namespace
+}  // namespace mitopk
+
+MI_TOPK_EXPORT int topk_indices_noalloc(const float* logits, int64_t row_stride, const int32_t* lengths,
+                                        int64_t num_rows, int32_t k, int32_t* out, hipStream_t stream) {
+  int st = check_shape(num_rows, row_stride, k);
+  if (st != MI_TOPK_OK) return st;
+  if (num_rows == 0) return MI_TOPK_OK;
+  if (!logits || !lengths || !out) return MI_TOPK_EINVAL;
+  DeviceInfo dev;
+  if (device_info(&dev) != hipSuccess) return MI_TOPK_ELAUNCH;
+  if ((reinterpret_cast<uintptr_t>(logits) & 3u) || (reinterpret_cast<uintptr_t>(lengths) & 3u) ||
+      (reinterpret_cast<uintptr_t>(out) & 3u))
+    return MI_TOPK_EINVAL;
+  const int head_max = ((reinterpret_cast<uintptr_t>(logits) & 15u) == 0 && (row_stride & 3) == 0) ? 0 : 3;
+  Plan pl;
+  st = make_plan(num_rows, row_stride, k, MI_TOPK_PATH_AUTO, 0, head_max, dev, &pl);
+  if (st != MI_TOPK_OK) return st;
+  if (pl.ws_bytes > kScratchBytes) return MI_TOPK_ESCRATCH;
+  uint8_t* ws = nullptr;
+  st = scratch_of(stream, &ws);
+  if (st != MI_TOPK_OK) return st;
+  // The split path's cross-workgroup waits are bounded; one that gives up
+  // leaves its row's counters behind, so that path starts from a cleared
+  // region.  The other paths leave the scratch zero whatever the data.
+  if (kKinds[pl.kind].mode == kModeSplit) {
+    st = fill_zero(ws, pl.ws_bytes, stream);
+    if (st != MI_TOPK_OK) return st;
+  }
+  return topk_impl(logits, row_stride, lengths, num_rows, k, out, ws, kScratchBytes,
+                   MI_TOPK_PATH_AUTO, 0, stream);
 }
