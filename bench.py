@@ -11,11 +11,14 @@ each launch gives the spread of single launches.  For context the line also
 carries `read_ceiling`: a plain max (torch.amax) over the same bytes and input
 copies (rows cut into pieces when there are few), timed the same way, i.e.
 what a simple streaming read of the batch reaches on this GPU (also for the
-secondary workload, with the secondary's copy-calibrated HBM traffic);
+long-context workload in `configs`);
 `warm_cache`: the same launches on one reused input copy; `paged_output`:
 the same launches writing KV-cache slots through a page table (the index
 transform fused into the stores); and `value_order`: the selection followed by
-the kernel that ranks each row's columns by value.  Prints one JSON line.
+the kernel that ranks each row's columns by value.  `configs` times the
+other four workloads the same way (long with its own read ceiling), and
+`c128a_metadata` the C128A metadata kernel at the shapes the adaptive-width
+page times.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload prefill]
 """
@@ -82,6 +85,15 @@ def measured_traffic(workload: str):
 _CPU = {}
 
 
+def cpu_share() -> int:
+    """Host threads this process may keep busy: the OMP_NUM_THREADS the
+    machine sets for one GPU's share of its cores (16 if unset)."""
+    try:
+        return max(1, int(os.environ.get("OMP_NUM_THREADS", "16")))
+    except ValueError:
+        return 16
+
+
 def _oracle_rows(rows):
     from oracle import oracle_topk_row, row_view
     w = _CPU["w"]
@@ -94,7 +106,8 @@ def _oracle_rows(rows):
 
 def cpu_baseline(w, max_rows: int) -> dict:
     """The CPU oracle, as it stands, over a bounded sample of the same rows."""
-    cores = min(16, len(os.sched_getaffinity(0)))
+    affinity = len(os.sched_getaffinity(0))
+    cores = min(affinity, cpu_share())
     _CPU["w"] = w
     _CPU["flat"], _CPU["lengths"] = workloads.to_numpy(w)
     rows = list(range(min(max_rows, w.num_rows)))
@@ -109,6 +122,7 @@ def cpu_baseline(w, max_rows: int) -> dict:
     n1 = _oracle_rows(one)
     d1 = time.perf_counter() - t1
     return {"value": done / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "affinity_cores": affinity,
             "sample": f"first {done} rows of the {w.name} workload, one pass, "
                       f"numpy stable argsort per row across a {cores}-process pool "
                       f"({dt:.2f} s wall)",
@@ -271,21 +285,112 @@ def calibrate_copy() -> None:
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 5}), flush=True)
 
 
+# The page's own timings of the C128A metadata build (context 32768, capacity
+# 8192, active width 256; Triton do_bench medians, hardware not stated):
+# tokens -> (fixed-width us, adaptive-width us).
+C128A_PAGE_US = {512: (9.22, 7.20), 2048: (15.39, 7.20), 8192: (44.00, 11.30), 32768: (150.56, 25.79)}
+
+
+def time_c128a(steps: int, warmup: int) -> dict:
+    """The C128A metadata kernel at the page's shapes: prefill tokens at
+    positions 32768 - T .. 32767, capacity 8192, the fixed width (8192)
+    and the adaptive width (256).  `us`: launches back to back between two
+    events through the C ABI with the arguments marshalled once (so the
+    figure is the GPU's, not Python's); `us_single`: the median of an event
+    pair around each launch, as the page's do_bench times one call."""
+    import ctypes
+    import row_wise_top_topk_amd as mt
+    lib = mt.load_library()
+    dev = torch.device("cuda:0")
+    context, ratio, capacity = 32768, 128, 8192
+    active = mt.c128a_active_width(context, ratio)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    rows = []
+    for T in sorted(C128A_PAGE_US):
+        pos = torch.arange(context - T, context, dtype=torch.int64, device=dev)
+        pbuf = torch.empty((T, capacity), dtype=torch.int32, device=dev)
+        for label, width, page_us in (("fixed", capacity, C128A_PAGE_US[T][0]),
+                                      ("adaptive", active, C128A_PAGE_US[T][1])):
+            args = (ctypes.c_void_p(pos.data_ptr()), T, ratio, 0, None, None, 0, 2, None, 0, None,
+                    ctypes.c_void_p(pbuf.data_ptr()), capacity, width, sp)
+            fn = lib.c128a_topk_metadata
+            for _ in range(warmup):
+                if fn(*args) != 0:
+                    raise RuntimeError("c128a_topk_metadata failed")
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                fn(*args)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / steps * 1e3
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(steps)]
+            for a, b in pairs:
+                a.record(stream)
+                fn(*args)
+                b.record(stream)
+            torch.cuda.synchronize()
+            single = float(np.median([a.elapsed_time(b) for a, b in pairs])) * 1e3
+            nbytes = 4 * T * width + 8 * T       # rows written, positions read
+            rows.append({"tokens": T, "width": label, "entries_per_row": width, "us": us,
+                         "us_single": single, "gbs": nbytes / (us * 1e-6) / 1e9,
+                         "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         "page_us": page_us})
+        del pbuf
+    return {"kernel": "c128a_metadata_kernel", "context": context, "compress_ratio": ratio,
+            "capacity": capacity, "active_width": active, "rows": rows,
+            "note": "page_us: the page's Triton do_bench medians (hardware not stated), context only"}
+
+
+def time_config(name: str, steps: int, warmup: int, with_read_ceiling: bool = False) -> dict:
+    """One named workload through the automatic path, cold inputs, K launches
+    back to back between two events."""
+    w = workloads.make(name)
+    c = input_copies(w)
+    t, pl, _ = time_workload(w, steps, warmup, copies=c)
+    b = w.algorithmic_bytes()
+    m = t / steps
+    res = {"workload": DESCRIPTIONS[name], "input_copies": c, "rows": w.num_rows,
+           "row_stride": w.row_stride, "k": w.k, "valid_elements": w.valid_elements,
+           "rows_with_length_below_k": int((w.lengths.to(torch.int64).clamp(0, w.row_stride)
+                                            < w.k).sum()),
+           "algorithmic_bytes": b,
+           "launch_us_mean": m * 1e3,
+           "launch_us_p50": float(np.percentile(pl, 50)) * 1e3,
+           "rows_per_s": w.num_rows / (m * 1e-3),
+           "achieved_gbs": b / (m * 1e-3) / 1e9,
+           "frac": b / (m * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "traffic": measured_traffic(name)}
+    if with_read_ceiling:
+        rc = read_ceiling(w, steps, warmup, c)
+        res["read_ceiling"] = {"us_per_launch": rc["us_per_launch"], "gbs": rc["gbs"], "frac": rc["frac"],
+                               "topk_over_read_time": m * 1e3 / rc["us_per_launch"]}
+    return res
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--secondary", default="long",
-                    help="a second workload timed for context ('' to skip)")
+    ap.add_argument("--others", default="long,decode,adversarial,tiny",
+                    help="the other workloads timed for the line's `configs` ('' to skip)")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the workload the CPU oracle leg processes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip paged output, value order, warm cache, read ceiling and C128A")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB five times (HBM counter calibration)")
     ap.add_argument("--rows-sweep", action="store_true",
                     help="only time the workload at several row counts and fit time against rows")
+    ap.add_argument("--c128a-only", action="store_true",
+                    help="only time the C128A metadata kernel at the page's shapes")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
@@ -297,6 +402,9 @@ def main() -> None:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): rows are independent, "
               "so the path shards by rows with no exchange; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.c128a_only:
+        print(json.dumps(time_c128a(args.steps, args.warmup)), flush=True)
+        return
 
     w = workloads.make(args.workload)
     cpu = None
@@ -344,42 +452,31 @@ def main() -> None:
         "host_wall_s": wall,
         "env": gpu_env(),
     }
-    if args.secondary and args.secondary != args.workload:
-        w2 = workloads.make(args.secondary)
-        c2 = input_copies(w2)
-        t2, pl2, _ = time_workload(w2, args.steps, args.warmup, copies=c2)
-        b2 = w2.algorithmic_bytes()
-        m2 = t2 / args.steps
-        result["secondary"] = {"workload": DESCRIPTIONS[args.secondary], "input_copies": c2,
-                               "launch_us_mean": m2 * 1e3,
-                               "launch_us_p50": float(np.percentile(pl2, 50)) * 1e3,
-                               "rows_per_s": w2.num_rows / (t2 / args.steps * 1e-3),
-                               "achieved_gbs": b2 / (m2 * 1e-3) / 1e9,
-                               "frac": b2 / (m2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                               "traffic": measured_traffic(args.secondary)}
-        rc2 = read_ceiling(w2, args.steps, args.warmup, c2)
-        result["secondary"]["read_ceiling"] = {"us_per_launch": rc2["us_per_launch"],
-                                               "gbs": rc2["gbs"], "frac": rc2["frac"],
-                                               "topk_over_read_time": m2 * 1e3 / rc2["us_per_launch"]}
-    paged_ms, _, _ = time_workload(w, args.steps, args.warmup, copies=copies, paging=paging_for(w))
-    result["paged_output"] = {"page_size": 64, "requests": 1,
-                              "launch_us_mean": paged_ms / args.steps * 1e3,
-                              "over_plain_us": (paged_ms / args.steps - avg_launch_ms) * 1e3,
-                              "note": "topk_indices_paged: columns written as KV-cache slots "
-                                      "through a random page table, fused into the stores"}
-    vo_ms, _, _ = time_workload(w, args.steps, args.warmup, copies=copies, order="value")
-    result["value_order"] = {"launch_us_mean": vo_ms / args.steps * 1e3,
-                             "over_plain_us": (vo_ms / args.steps - avg_launch_ms) * 1e3,
-                             "note": "topk_indices(order='value'): the selection, then "
-                                     "topk_value_order ranking each row's columns by value"}
-    warm_ms, _, _ = time_workload(w, args.steps, args.warmup, copies=1)
-    result["warm_cache"] = {"input_copies": 1, "launch_us_mean": warm_ms / args.steps * 1e3,
-                            "achieved_gbs": alg_bytes / (warm_ms / args.steps * 1e-3) / 1e9,
-                            "note": "one input copy reused: parts of it may be served from the caches"}
-    rc = read_ceiling(w, args.steps, args.warmup, copies)
-    rc["topk_over_read_time"] = avg_launch_ms * 1e3 / rc["us_per_launch"]
-    rc["topk_gbs_over_read_gbs"] = achieved / rc["gbs"]
-    result["read_ceiling"] = rc
+    others = [n for n in args.others.split(",") if n and n != args.workload]
+    if others:
+        result["configs"] = {n: time_config(n, args.steps, args.warmup, with_read_ceiling=(n == "long"))
+                             for n in others}
+    if not args.no_extras:
+        paged_ms, _, _ = time_workload(w, args.steps, args.warmup, copies=copies, paging=paging_for(w))
+        result["paged_output"] = {"page_size": 64, "requests": 1,
+                                  "launch_us_mean": paged_ms / args.steps * 1e3,
+                                  "over_plain_us": (paged_ms / args.steps - avg_launch_ms) * 1e3,
+                                  "note": "topk_indices_paged: columns written as KV-cache slots "
+                                          "through a random page table, fused into the stores"}
+        vo_ms, _, _ = time_workload(w, args.steps, args.warmup, copies=copies, order="value")
+        result["value_order"] = {"launch_us_mean": vo_ms / args.steps * 1e3,
+                                 "over_plain_us": (vo_ms / args.steps - avg_launch_ms) * 1e3,
+                                 "note": "topk_indices(order='value'): the selection with each "
+                                         "row's columns ranked by value"}
+        warm_ms, _, _ = time_workload(w, args.steps, args.warmup, copies=1)
+        result["warm_cache"] = {"input_copies": 1, "launch_us_mean": warm_ms / args.steps * 1e3,
+                                "achieved_gbs": alg_bytes / (warm_ms / args.steps * 1e-3) / 1e9,
+                                "note": "one input copy reused: parts of it may be served from the caches"}
+        rc = read_ceiling(w, args.steps, args.warmup, copies)
+        rc["topk_over_read_time"] = avg_launch_ms * 1e3 / rc["us_per_launch"]
+        rc["topk_gbs_over_read_gbs"] = achieved / rc["gbs"]
+        result["read_ceiling"] = rc
+        result["c128a_metadata"] = time_c128a(args.steps, args.warmup)
     print(json.dumps(result), flush=True)
 
 

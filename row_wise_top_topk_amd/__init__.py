@@ -18,6 +18,7 @@ __all__ = [
     "PATH_AUTO", "PATH_LOCAL", "PATH_SPLIT", "PATH_CHUNKS",
     "library_path", "load_library", "topk_indices", "workspace_size",
     "plan_describe", "debug_keys", "workspace_error", "status_string",
+    "c128a_active_width", "c128a_topk_metadata",
 ]
 
 PATH_AUTO, PATH_LOCAL, PATH_SPLIT, PATH_CHUNKS = 0, 1, 2, 3
@@ -62,6 +63,10 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.topk_debug_keys.restype = ctypes.c_int
     lib.topk_indices_noalloc.argtypes = [vp, i64, vp, i64, i32, vp, vp]
     lib.topk_indices_noalloc.restype = ctypes.c_int
+    lib.c128a_active_width.argtypes = [i64, i32]
+    lib.c128a_active_width.restype = i32
+    lib.c128a_topk_metadata.argtypes = [vp, i64, i32, i64, vp, vp, i64, i32, vp, i64, vp, vp, i64, i32, vp]
+    lib.c128a_topk_metadata.restype = ctypes.c_int
     return lib
 
 
@@ -264,3 +269,59 @@ def debug_keys(x: torch.Tensor) -> torch.Tensor:
         _check(load_library().topk_debug_keys(x.data_ptr(), out.data_ptr(), x.numel(), stream),
                "topk_debug_keys")
     return out
+
+
+def c128a_active_width(context_len: int, compress_ratio: int = 128) -> int:
+    """The adaptive C128A width, max(next_pow2(context_len // compress_ratio), 128)."""
+    w = int(load_library().c128a_active_width(int(context_len), int(compress_ratio)))
+    if w < 0:
+        raise ValueError("context_len must be >= 0 and compress_ratio >= 1")
+    return w
+
+
+def c128a_topk_metadata(positions: torch.Tensor, compress_ratio: int, num_decode_tokens: int,
+                        token_to_req: torch.Tensor, block_table: torch.Tensor, block_size: int,
+                        decode_buf: torch.Tensor, decode_lens: torch.Tensor,
+                        prefill_buf: torch.Tensor, width: int) -> None:
+    """The C128A index rows (c128a_topk_metadata in mi_c128a.h): writes the
+    first ``width`` entries of every row of ``decode_buf`` (the first
+    ``num_decode_tokens`` tokens: KV-cache slots through ``block_table``) and
+    ``prefill_buf`` (the other tokens: entry numbers), and ``decode_lens``;
+    the buffers' row strides (the capacity) are kept.  ``positions`` int64
+    [tokens]; ``token_to_req`` int32 [tokens]; ``block_table`` int32
+    [requests, pages]; the buffers int32 2-D with unit stride along their
+    last axis.  Decode arguments may be None when there are no decode tokens."""
+    lib = load_library()
+    dev = positions.device
+    if positions.dtype != torch.int64 or positions.dim() != 1 or not positions.is_contiguous():
+        raise ValueError("positions must be a contiguous 1-D int64 tensor")
+    T = int(positions.shape[0])
+    nd = int(num_decode_tokens)
+
+    def ptr(t, dtype, what, dims):
+        if t is None:
+            return None, 0
+        if t.dtype != dtype or t.dim() != dims or t.device != dev:
+            raise ValueError(f"{what} must be a {dims}-D {dtype} tensor on the positions' device")
+        if dims == 2 and t.shape[1] > 1 and t.stride(1) != 1:
+            raise ValueError(f"{what} must have unit stride along its last axis")
+        if dims == 1 and not t.is_contiguous():
+            raise ValueError(f"{what} must be contiguous")
+        return t.data_ptr(), (int(t.stride(0)) if dims == 2 else 0)
+
+    tr, _ = ptr(token_to_req, torch.int32, "token_to_req", 1)
+    bt, bts = ptr(block_table, torch.int32, "block_table", 2)
+    db, ds = ptr(decode_buf, torch.int32, "decode_buf", 2)
+    dl, _ = ptr(decode_lens, torch.int32, "decode_lens", 1)
+    pb, ps = ptr(prefill_buf, torch.int32, "prefill_buf", 2)
+    if nd > 0 and None not in (decode_buf, decode_lens, token_to_req) and (
+            decode_buf.shape[0] < nd or decode_lens.shape[0] < nd or token_to_req.shape[0] < nd):
+        raise ValueError("decode buffers must have a row per decode token")
+    if T > nd and prefill_buf.shape[0] < T - nd:
+        raise ValueError("prefill_buf must have a row per prefill token")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = lib.c128a_topk_metadata(positions.data_ptr(), T, int(compress_ratio), nd, tr, bt, bts,
+                                     int(block_size), db, ds, dl, pb, ps, int(width), stream)
+    if st != 0:
+        raise RuntimeError(f"c128a_topk_metadata failed (status {st})")

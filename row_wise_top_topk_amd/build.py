@@ -19,7 +19,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = [os.path.join(CSRC, "topk_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "topk_kernels.hip"), os.path.join(CSRC, "c128a_metadata.hip")]
 LIB = os.path.join(PKG, "libmi_topk.so")
 LIB_O1 = os.path.join(PKG, "libmi_topk_O1.so")
 ARCH = "gfx950"

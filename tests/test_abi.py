@@ -4,6 +4,7 @@ No GPU needed: only calls that return before touching a device are made.
 """
 
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -11,14 +12,17 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mi_topk.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("mi_topk.h", "mi_c128a.h")]
+PREFIXES = ("topk_", "c128a_")
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
-    keep = [n for n in names if n.startswith("topk_")]
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    keep = [n for n in names if n.startswith(PREFIXES)]
     return sorted(set(keep))
 
 
@@ -45,8 +49,9 @@ def test_every_declared_symbol_is_exported(lib):
     for n in _declared_functions():
         assert n in exported, n
         assert getattr(lib, n) is not None
-    # nothing else with C linkage leaks out under a topk_ name
-    assert {e for e in exported if e.startswith("topk_")} == set(_declared_functions())
+    # nothing else with C linkage leaks out under the library's prefixes
+    assert {e for e in exported if e.startswith(PREFIXES)} == set(_declared_functions())
+    assert set(glob.glob(os.path.join(ROOT, "include", "*.h"))) == set(HEADERS)
 
 
 def test_status_strings(lib):
@@ -82,3 +87,28 @@ def test_invalid_arguments_rejected_before_any_device_call(lib):
     assert vo(None, 8, fake, 3, 4, fake, None) == 1                      # NULL logits
     assert vo(fake, 8, fake, 3, 4, None, None) == 1                      # NULL idx
     assert vo(fake, 8, fake, 0, 4, fake, None) == 0                      # empty batch: no-op
+
+
+def test_c128a_width_rule_and_argument_checks(lib):
+    # host-only: the width rule, and calls rejected before anything is enqueued
+    assert lib.c128a_active_width(32768, 128) == 256
+    assert lib.c128a_active_width(9037, 128) == 128
+    assert lib.c128a_active_width(65536, 128) == 512
+    assert lib.c128a_active_width(-1, 128) == -1
+    assert lib.c128a_active_width(100, 0) == -1
+    vp = ctypes.c_void_p
+    fake = vp(0x1000)
+    call = lib.c128a_topk_metadata
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("pos", fake), ("T", 4), ("ratio", 128), ("nd", 0), ("tr", None), ("bt", None), ("bts", 0),
+        ("bs", 2), ("db", None), ("ds", 0), ("dl", None), ("pb", fake), ("ps", 8), ("w", 8), ("s", None))]
+    assert call(*args(T=0)) == 0                 # no tokens: no-op
+    assert call(*args(T=-1)) == 1
+    assert call(*args(ratio=0)) == 1
+    assert call(*args(w=0)) == 1
+    assert call(*args(ps=7)) == 1                # stride below the width
+    assert call(*args(nd=5)) == 1                # more decode tokens than tokens
+    assert call(*args(nd=2)) == 1                # decode tokens without decode buffers
+    assert call(*args(pos=None)) == 1
+    assert call(*args(pos=vp(0x1004))) == 1      # positions not 8-byte aligned
+    assert call(*args(pb=None)) == 1
