@@ -183,6 +183,25 @@ int topk_value_order(const float* logits, int64_t row_stride, const int32_t* len
                      int64_t num_rows, int32_t k, int32_t* idx, hipStream_t stream);
 
 /*
+ * topk_indices() / topk_indices_path() with the output in value order: the
+ * first m = min(k, L_i) entries of each row run from the largest value to
+ * the smallest, equal values by ascending column (the set is the same);
+ * slots [m, k) hold -1.  The register, streaming and chunked kernels rank the
+ * selected entries in their own emission (their keys are on chip, or the row
+ * was just read): the composites (key, reversed column) of a row are sorted
+ * in LDS.  The cooperative split kernel is followed by the topk_value_order
+ * pass.  1 <= k <= 4096; no page table.  Everything else as topk_indices().
+ */
+int topk_indices_sorted(const float* logits, int64_t row_stride, const int32_t* lengths,
+                        int64_t num_rows, int32_t k, int32_t* out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+int topk_indices_sorted_path(const float* logits, int64_t row_stride, const int32_t* lengths,
+                             int64_t num_rows, int32_t k, int32_t* out, void* workspace,
+                             size_t workspace_bytes, int32_t path, int32_t chunks,
+                             hipStream_t stream);
+
+/*
  * Describe the launch topk_indices_path() would make, without launching:
  * writes up to 7 int64 values to `info` (path, block threads, elements per
  * thread, chunk elements, chunks per row, grid workgroups, workspace bytes)

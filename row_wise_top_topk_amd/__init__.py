@@ -61,6 +61,10 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.topk_value_order.restype = ctypes.c_int
     lib.topk_debug_keys.argtypes = [vp, vp, i64, vp]
     lib.topk_debug_keys.restype = ctypes.c_int
+    lib.topk_indices_sorted.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, vp]
+    lib.topk_indices_sorted.restype = ctypes.c_int
+    lib.topk_indices_sorted_path.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, i32, i32, vp]
+    lib.topk_indices_sorted_path.restype = ctypes.c_int
     lib.topk_indices_noalloc.argtypes = [vp, i64, vp, i64, i32, vp, vp]
     lib.topk_indices_noalloc.restype = ctypes.c_int
     lib.c128a_active_width.argtypes = [i64, i32]
@@ -177,7 +181,8 @@ def topk_indices(logits: torch.Tensor, lengths: torch.Tensor, k: int, out: torch
 
     ``order="value"`` returns each row's selected columns from the largest
     value to the smallest (equal values by ascending column) instead of in
-    ascending column order (k <= 4096, not with a page table).
+    ascending column order, ranked inside the selection kernels
+    (topk_indices_sorted_path; k <= 4096, not with a page table).
 
     ``library``: path of another build of the library to call (default: the
     in-tree ``libmi_topk.so``).
@@ -221,15 +226,11 @@ def topk_indices(logits: torch.Tensor, lengths: torch.Tensor, k: int, out: torch
             workspace = _cached_workspace(device, stream, need)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     if block_table is None:
+        fn = lib.topk_indices_sorted_path if order == "value" else lib.topk_indices_path
         with torch.cuda.device(device):
-            st = lib.topk_indices_path(logits.data_ptr(), row_stride, lengths.data_ptr(), rows, k,
-                                       out.data_ptr(), ws_ptr, ws_bytes, pid, int(chunks), stream)
+            st = fn(logits.data_ptr(), row_stride, lengths.data_ptr(), rows, k,
+                    out.data_ptr(), ws_ptr, ws_bytes, pid, int(chunks), stream)
         _check(st, "topk_indices")
-        if order == "value":
-            with torch.cuda.device(device):
-                st = lib.topk_value_order(logits.data_ptr(), row_stride, lengths.data_ptr(), rows, k,
-                                          out.data_ptr(), stream)
-            _check(st, "topk_value_order")
     else:
         if (block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.device != device
                 or (block_table.shape[1] > 1 and block_table.stride(1) != 1)):
@@ -325,3 +326,16 @@ def c128a_topk_metadata(positions: torch.Tensor, compress_ratio: int, num_decode
                                      int(block_size), db, ds, dl, pb, ps, int(width), stream)
     if st != 0:
         raise RuntimeError(f"c128a_topk_metadata failed (status {st})")
+
+
+def value_order(logits: torch.Tensor, lengths: torch.Tensor, idx: torch.Tensor) -> torch.Tensor:
+    """Reorder an existing selection ``idx`` (int32 [rows, k], the output of
+    topk_indices for the same logits and lengths) by value, in place
+    (topk_value_order: a separate pass that reads the selected values back)."""
+    rows, k = int(idx.shape[0]), int(idx.shape[1])
+    row_stride = int(logits.stride(0)) if rows > 1 else max(int(logits.stride(0)), int(logits.shape[1]), 1)
+    stream = torch.cuda.current_stream(logits.device).cuda_stream
+    with torch.cuda.device(logits.device):
+        _check(load_library().topk_value_order(logits.data_ptr(), row_stride, lengths.data_ptr(), rows, k,
+                                               idx.data_ptr(), stream), "topk_value_order")
+    return idx

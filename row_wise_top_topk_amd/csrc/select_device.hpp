@@ -105,6 +105,11 @@ struct PredIdx {    // bits > 32: key == T decided, index digits follow
   }
 };
 
+// The smallest key an entry selected by prefix p can have.
+__device__ __forceinline__ uint32_t prefix_edge(const Prefix& p) {
+  return p.bits >= 32 ? p.kp : (p.kp << (32 - p.bits));
+}
+
 // Calls f(pred) with the prefix test for p (a uniform branch).
 template <class F>
 __device__ __forceinline__ void with_pred(const Prefix& p, int ib, uint32_t rmask, F f) {
@@ -475,6 +480,215 @@ __device__ __forceinline__ Prefix rounds_window(const Src& src, uint32_t lo, uin
   if (cnt == need) return p;
   if (cnt <= static_cast<uint32_t>(kWave)) return finish_small<BLOCK>(src, base + b, s, need, ib, hist, res);
   return rounds_local<BLOCK>(src, p, need, ib, hist, res, wt);
+}
+
+}  // namespace mitopk
+
+namespace mitopk {
+
+// ---------------------------------------------------------------------------
+// Value order: a row's selected columns ranked from the largest value to the
+// smallest, equal values by ascending column.  Each selected entry becomes
+// the 64-bit composite (key << 32) | (2^32 - 1 - column), distinct per entry,
+// whose descending order is exactly that ranking; the composites of a row
+// are sorted in LDS by a bitonic network.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t vo_composite(uint32_t key, int32_t j) {
+  return (static_cast<uint64_t>(key) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(j));
+}
+__device__ __forceinline__ int32_t vo_column(uint64_t c) {
+  return static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(c));
+}
+
+// Sorts a[0..n) descending, n a power of two, every thread of the workgroup
+// taking part (the caller synchronises before, so a[] is complete).  Thread t
+// handles pairs t, t + BLOCK, ...: pair p of stride s compares elements
+// i = 2p - (p mod s) and i + s.  For s <= 64 the pairs of wavefront w lie in
+// its own 128-element slices ([128w, 128w + 128) + 2*BLOCK*r), the same
+// slices at every such stride, so consecutive stages of stride <= 64 need
+// only the wavefront's own ordering; a workgroup barrier separates a stage
+// from its neighbours only where one of them has a larger stride.
+template <int BLOCK>
+__device__ __forceinline__ void bitonic_sort_desc(uint64_t* a, int n) {
+  const int tid = static_cast<int>(threadIdx.x);
+  bool prev_wide = false;
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int s = size >> 1; s > 0; s >>= 1) {
+      const bool wide = s > 64;
+      if (wide || prev_wide) {
+        __syncthreads();
+      } else {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+      prev_wide = wide;
+      for (int p = tid; p < (n >> 1); p += BLOCK) {
+        const int i = ((p & ~(s - 1)) << 1) | (p & (s - 1));
+        const uint64_t x = a[i], y = a[i + s];
+        const bool desc = (i & size) == 0;
+        if (desc ? x < y : x > y) {
+          a[i] = y;
+          a[i + s] = x;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// comp[0..m) holds a row's selected composites (in any order): sorts them
+// and writes their columns to out[0..m).  comp must hold next_pow2(m)
+// entries.
+template <int BLOCK>
+__device__ __forceinline__ void vo_sort_store(uint64_t* comp, int m, int32_t* out) {
+  if (m <= 0) return;
+  int n = 1;
+  while (n < m) n <<= 1;
+  for (int i = m + static_cast<int>(threadIdx.x); i < n; i += BLOCK) comp[i] = 0ull;  // sorts last
+  __syncthreads();
+  bitonic_sort_desc<BLOCK>(comp, n);
+  for (int i = static_cast<int>(threadIdx.x); i < m; i += BLOCK) out[i] = vo_column(comp[i]);
+}
+
+// Ranks by value the m columns this workgroup has just written to out[0..m)
+// of a row (its first L entries at `row`): the values are read back from the
+// row, which the workgroup has just streamed, so they come from the caches.
+template <int BLOCK>
+__device__ __forceinline__ void vo_rank_written(const float* row, int L, int m, int32_t* out,
+                                                uint64_t* comp) {
+  if (m <= 1) return;
+  __syncthreads();  // the workgroup's stores to out are visible to its loads
+  for (int i = static_cast<int>(threadIdx.x); i < m; i += BLOCK) {
+    const int32_t j = out[i];
+    const uint32_t key = (j >= 0 && j < L) ? order_key(row[j]) : 0u;
+    comp[i] = vo_composite(key, j);
+  }
+  vo_sort_store<BLOCK>(comp, m, out);
+}
+
+}  // namespace mitopk
+
+namespace mitopk {
+
+// The float value of an order-preserving key (the inverse of order_key).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : (0u - key));
+}
+
+// A monotone map from keys in [lo, hi] to 4096 bins (a larger key never gets
+// a smaller bin), spreading the values of a row's selected entries evenly:
+// linear in the value, (x - x_lo) * 4096 / (x_hi - x_lo), which rounding
+// keeps monotone; NaN keys (above +inf, below -inf) take the end bins.  When
+// a bound is infinite or the range overflows, the keys' 12-bit window below
+// the bits lo and hi share is used instead (linear in the key).
+struct VoBins {
+  static constexpr uint32_t kKeyPosInf = 0xFF800000u;  // key of +inf
+  static constexpr uint32_t kKeyNegInf = 0x00800000u;  // key of -inf
+  bool linear;
+  float xlo, scale;
+  int s;
+  uint32_t base;
+  __device__ __forceinline__ VoBins(uint32_t lo, uint32_t hi) {
+    xlo = key_value(lo);
+    const float xhi = key_value(hi);
+    const float span = xhi - xlo;
+    linear = lo >= kKeyNegInf && hi <= kKeyPosInf && __builtin_isfinite(xlo) && __builtin_isfinite(xhi) &&
+             __builtin_isfinite(span) && span > 0.0f;
+    scale = linear ? static_cast<float>(kFirstBins) / span : 0.0f;
+    s = 0;
+    while ((hi >> s) - (lo >> s) >= static_cast<uint32_t>(kFirstBins)) ++s;
+    base = lo >> s;
+  }
+  __device__ __forceinline__ uint32_t operator()(uint32_t key) const {
+    if (!linear) return (key >> s) - base;
+    if (key > kKeyPosInf) return kFirstBins - 1;
+    if (key < kKeyNegInf) return 0u;
+    const float v = (key_value(key) - xlo) * scale;
+    return static_cast<uint32_t>(fminf(fmaxf(v, 0.0f), static_cast<float>(kFirstBins - 1)));
+  }
+};
+
+// Value order for m selected entries whose keys all lie in [lo, hi], by
+// buckets instead of a sort (VoBins: 4096 bins in key order).  A count per
+// bin, a suffix scan (bins from the top: each bin's first rank), a scatter
+// of the composites through per-bin cursors, then each entry's rank among
+// the few entries of its own bin, by comparing composites.  A bin of more
+// than 64 entries (runs of equal or close values) sends the row through the
+// bitonic sort of the scattered composites instead.  for_each(f) calls
+// f(key, column) for each selected entry this thread holds (every entry
+// once in the workgroup; called twice).  word: 4096 LDS words; comp:
+// next_pow2(m) LDS composites; wt: BLOCK/64 words; res: 1 word.  Every
+// thread must call it; it synchronises first, so the caller may have read
+// any of these just before.
+template <int BLOCK, class ForEach>
+__device__ __forceinline__ void vo_bucket_rank(ForEach for_each, uint32_t lo, uint32_t hi, int m,
+                                               int32_t* out, uint32_t* word, uint64_t* comp,
+                                               uint32_t* wt, uint32_t* res) {
+  constexpr int NB = kFirstBins;
+  constexpr int NW = BLOCK / kWave;
+  constexpr int GS = NB / BLOCK;  // bins per thread in the scan
+  static_assert(GS >= 4 && GS % 4 == 0, "16-byte scan reads");
+  const int tid = static_cast<int>(threadIdx.x);
+  const VoBins bin_of(lo, hi);
+  __syncthreads();
+  for (int i = tid; i < NB; i += BLOCK) word[i] = 0u;
+  if (tid == 0) res[0] = 0u;
+  __syncthreads();
+  for_each([&](uint32_t key, int32_t) { atomicAdd(&word[bin_of(key)], 1u); });
+  __syncthreads();
+  // thread t: bins [NB - GS(t+1), NB - GS t), the top ones first (read
+  // twice rather than held, to keep registers free)
+  const int top = NB - tid * GS;
+  uint32_t sum = 0, mx = 0;
+#pragma unroll
+  for (int v = 0; v < GS / 4; ++v) {
+    const uint4 q = *reinterpret_cast<const uint4*>(word + top - 4 * (v + 1));
+    sum += q.x + q.y + q.z + q.w;
+    mx = max(max(mx, max(q.x, q.y)), max(q.z, q.w));
+  }
+  const uint32_t incl = wave_inclusive_sum(sum);
+  mx = wave_max(mx);
+  const int w = tid / kWave;
+  if ((tid & (kWave - 1)) == kWave - 1) wt[w] = incl;
+  if ((tid & (kWave - 1)) == 0) atomicMax(res, mx);
+  __syncthreads();
+  uint32_t run = incl - sum;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) run += v < w ? wt[v] : 0u;
+#pragma unroll
+  for (int v = 0; v < GS / 4; ++v) {  // each bin's first rank (bins from the top)
+    uint4* at = reinterpret_cast<uint4*>(word + top - 4 * (v + 1));
+    const uint4 q = *at;
+    uint4 o;
+    o.w = run;
+    o.z = o.w + q.w;
+    o.y = o.z + q.z;
+    o.x = o.y + q.y;
+    run = o.x + q.x;
+    *at = o;
+  }
+  const bool heavy = res[0] > static_cast<uint32_t>(kWave);
+  __syncthreads();
+  for_each([&](uint32_t key, int32_t j) {
+    comp[atomicAdd(&word[bin_of(key)], 1u)] = vo_composite(key, j);
+  });
+  if (heavy) {
+    vo_sort_store<BLOCK>(comp, m, out);  // (synchronises first)
+    return;
+  }
+  __syncthreads();
+  // after the scatter word[b] is the end of bin b and word[b + 1] its start
+#pragma unroll 1
+  for (int q = tid; q < m; q += BLOCK) {
+    const uint64_t c = comp[q];
+    const uint32_t b = bin_of(static_cast<uint32_t>(c >> 32));
+    const uint32_t start = b + 1 < static_cast<uint32_t>(NB) ? word[b + 1] : 0u;
+    const uint32_t end = word[b];
+    uint32_t r = start;
+    for (uint32_t t = start; t < end; ++t) r += comp[t] > c ? 1u : 0u;
+    out[r] = vo_column(c);
+  }
 }
 
 }  // namespace mitopk

@@ -42,6 +42,7 @@ namespace mitopk {
 namespace {
 
 constexpr int kCandCap = 4096;     // candidate list entries (split path)
+constexpr int kSortMaxK = 4096;    // largest k of a value-ordered selection (composites in LDS)
 constexpr int kMaxChunks = 1024;   // workgroups per row (split path)
 constexpr uint32_t kSpinLimit = 1u << 22;
 
@@ -581,23 +582,29 @@ __device__ __forceinline__ void select_row(uint32_t (&raw)[E], const Chunk& ch, 
 // ---------------------------------------------------------------------------
 // Two workgroups per CU (4 wavefronts per SIMD) let one workgroup's loads
 // overlap the other's selection.
-template <int BLOCK, int E>
+// VO: the selected columns leave ranked by value (their composites sorted in
+// LDS) instead of in ascending column order.
+template <int BLOCK, int E, bool VO>
 __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 topk_row_kernel(Params p) {
   __shared__ RowLds<BLOCK> lds;
+  static_assert(sizeof(RowLds<BLOCK>) >= 8 * kSortMaxK, "composites of a row fit the LDS");
   const int64_t row = blockIdx.x;
   const int L = row_length(p, row);
   const OutRow out_row = out_row_of(p, row);
+  const float* row_ptr = p.logits + row * p.row_stride;
+  uint64_t* comp = reinterpret_cast<uint64_t*>(&lds);
   if (L <= p.k) {
     write_trivial(out_row, L, p.k, BLOCK);
+    if constexpr (VO) vo_rank_written<BLOCK>(row_ptr, L, L, out_row.p, comp);
     return;
   }
-  const float* row_ptr = p.logits + row * p.row_stride;
   const int head = static_cast<int>((reinterpret_cast<uintptr_t>(row_ptr) >> 2) & 3u);
   const Chunk ch = make_chunk(row_ptr, head, 0, head, head + L);
   uint32_t raw[E];
   load_raw<BLOCK, E>(raw, ch);
   select_row<BLOCK, E>(raw, ch, L, p.k, out_row, lds);
+  if constexpr (VO) vo_rank_written<BLOCK>(row_ptr, L, p.k, out_row.p, comp);
 }
 
 // ---------------------------------------------------------------------------
@@ -808,19 +815,24 @@ __device__ __forceinline__ uint32_t filter_stream(const StreamGeom<BLOCK, NP>& g
   return cnt;
 }
 
-template <int BLOCK, int NP>
+template <int BLOCK, int NP, bool VO>
 __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(6)))
 topk_stream_kernel(Params p) {
   constexpr int NW = BLOCK / kWave;
   __shared__ StreamLds<BLOCK> lds;
+  // composites of a row; their bucket ranking: bins, staging, scatter (16 KB each)
+  static_assert(sizeof(lds.u) >= 8 * kSortMaxK && sizeof(lds.u) >= 12 * kFirstBins,
+                "composites of a row fit the LDS");
+  uint64_t* comp = reinterpret_cast<uint64_t*>(lds.u.list);
   const int64_t row = blockIdx.x;
   const int L = row_length(p, row);
   const OutRow out_row = out_row_of(p, row);
+  const float* row_ptr = p.logits + row * p.row_stride;
   if (L <= p.k) {
     write_trivial(out_row, L, p.k, BLOCK);
+    if constexpr (VO) vo_rank_written<BLOCK>(row_ptr, L, L, out_row.p, comp);
     return;
   }
-  const float* row_ptr = p.logits + row * p.row_stride;
   // word loads need no 16-byte alignment, so the row starts at element 0
   const Chunk ch = make_chunk(row_ptr, 0, 0, 0, L);
   const int ib = index_bits(L);
@@ -836,11 +848,13 @@ topk_stream_kernel(Params p) {
     const Prefix pf = rounds_local<BLOCK>(RegSource<BLOCK, kChunkPos>{key, ch}, Prefix{0, 0u, 0u},
                                           kk, ib, lds.u.hist, lds.res, lds.wtot);
     emit_ordered<BLOCK, kChunkPos>(key, ch, pf, ib, out_row, 0u, kk, lds.wtot);
+    if constexpr (VO) vo_rank_written<BLOCK>(row_ptr, L, p.k, out_row.p, comp);
     return;
   }
   const StreamGeom<BLOCK, NP> g(ch);
   if (L < 4 * p.k) {
     select_stream_exact<BLOCK, NP>(g, L, p.k, out_row, lds);
+    if constexpr (VO) vo_rank_written<BLOCK>(row_ptr, L, p.k, out_row.p, comp);
     return;
   }
 
@@ -898,6 +912,7 @@ topk_stream_kernel(Params p) {
   if (over || total < kk) {
     __syncthreads();  // wtot is reused
     select_stream_exact<BLOCK, NP>(g, L, p.k, out_row, lds);
+    if constexpr (VO) vo_rank_written<BLOCK>(row_ptr, L, p.k, out_row.p, comp);
     return;
   }
 
@@ -936,6 +951,13 @@ topk_stream_kernel(Params p) {
   // every listed key lies in [lb, largest]
   const uint32_t kmax = lds.res[3];
   const Prefix pf = rounds_window<BLOCK>(lst, lb, kmax, kk, ib, lds.u.hist, lds.res, lds.wtot);
+  // VO: with k <= 2048 the selected composites are staged in LDS at their
+  // column-order ranks (the list's registers end here) and ranked by value
+  // from there: union words [0, 16 KB) bins, [16, 32) staging, [32, 48) the
+  // scattered composites.  A larger k ranks the written row instead.
+  constexpr int kVoStage = kFirstBins / 2;
+  uint64_t* const stage = comp + kVoStage;
+  const bool vo_lds = VO && p.k <= kVoStage;
   with_pred(pf, ib, rmask, [&](const auto& pred) {
     uint32_t n = 0;
 #pragma unroll
@@ -947,11 +969,34 @@ topk_stream_kernel(Params p) {
 #pragma unroll
     for (int u = 0; u < kListPerThread; ++u) {
       if (pred.ge(lst.key[u], lst.col[u])) {
-        if (pos < kk) out_row.put(pos, lst.col[u]);
+        if (pos < kk) {
+          if (vo_lds) {
+            stage[pos] = vo_composite(lst.key[u], lst.col[u]);
+          } else {
+            out_row.put(pos, lst.col[u]);
+          }
+        }
         ++pos;
       }
     }
   });
+  if constexpr (VO) {
+    if (vo_lds) {
+      __syncthreads();  // the staged composites are complete
+      const int m = p.k;
+      vo_bucket_rank<BLOCK>(
+          [&](auto f) {
+#pragma unroll 1
+            for (int i = tid; i < m; i += BLOCK) {
+              const uint64_t c = stage[i];
+              f(static_cast<uint32_t>(c >> 32), vo_column(c));
+            }
+          },
+          prefix_edge(pf), kmax, m, out_row.p, lds.u.hist, comp + 2 * kVoStage, lds.wtot, lds.res);
+    } else {
+      vo_rank_written<BLOCK>(row_ptr, L, p.k, out_row.p, comp);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1428,11 +1473,15 @@ __device__ __forceinline__ void hist_add_entries(uint32_t* hist, BinOf bin_of, T
   }
 }
 
-template <int BLOCK, int E>
+template <int BLOCK, int E, bool VO>
 __global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 topk_chunks_kernel(Params p) {
   constexpr int NW = BLOCK / kWave;
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kFirstBins];
+  // the histogram's words; with VO also the composites of the row (32 KB)
+  // behind them
+  __shared__ __attribute__((aligned(16))) uint64_t hist_words[kFirstBins / 2 + (VO ? kSortMaxK : 0)];
+  uint32_t* const hist = reinterpret_cast<uint32_t*>(hist_words);
+  uint64_t* const comp = hist_words + kFirstBins / 2;
   __shared__ uint32_t coff[kMaxChunks + 1];
   __shared__ uint16_t scol[kChunkCap];
   __shared__ uint32_t wq[4 * NW];
@@ -1444,14 +1493,17 @@ topk_chunks_kernel(Params p) {
   const int g = static_cast<int>(blockIdx.x % G);
   const int L = row_length(p, row);
   const OutRow out_row = out_row_of(p, row);
+  const float* row_ptr = p.logits + row * p.row_stride;
   if (L <= p.k) {
-    if (g == 0) write_trivial(out_row, L, p.k, BLOCK);
+    if (g == 0) {
+      write_trivial(out_row, L, p.k, BLOCK);
+      if constexpr (VO) vo_rank_written<BLOCK>(row_ptr, L, L, out_row.p, comp);
+    }
     return;
   }
   const int chunk = BLOCK * E;
   const int Gr = (L + chunk - 1) / chunk;
   if (g >= Gr) return;
-  const float* row_ptr = p.logits + row * p.row_stride;
   const int64_t cbase = static_cast<int64_t>(g) * chunk;
   const int clen = static_cast<int>(L - cbase < chunk ? L - cbase : chunk);
   const Chunk ch = make_chunk(row_ptr, 0, cbase, 0, clen);
@@ -1465,6 +1517,7 @@ topk_chunks_kernel(Params p) {
     load_raw<BLOCK, E>(raw1, ch);
     keys_in_place<BLOCK, E>(raw1, ch);
     select_chunk_whole_row<BLOCK, E>(raw1, ch, L, p.k, out_row, hist, wtot, res);
+    if constexpr (VO) vo_rank_written<BLOCK>(row_ptr, L, p.k, out_row.p, comp);
     return;
   }
   // The chunk's raw bits, every load issued at once (past the row they read
@@ -1822,7 +1875,7 @@ topk_chunks_kernel(Params p) {
     // its words held the chunk map, rounds_window clears them
     const Prefix pf = rounds_window<BLOCK>(un, min_lb, kmax, kk, ib, hist, res, wtot, slotted);
     // every selected key is at least the selected bucket's lower edge
-    const uint32_t edge = pf.bits >= 32 ? pf.kp : (pf.kp << (32 - pf.bits));
+    const uint32_t edge = prefix_edge(pf);
     if (edge >= max_lb) {
       // ordered emission.  The union's order is (group q, wavefront, lane,
       // j), so a selected entry's rank is: the selected entries of the
@@ -1839,6 +1892,17 @@ topk_chunks_kernel(Params p) {
 #pragma unroll
         for (int u = 0; u < kUnionPerThread; ++u)
           sel |= pred.ge(un.key[u], un.col(u)) ? (1u << u) : 0u;
+        if constexpr (VO) {
+          // the selected keys are on chip: ranked by buckets of the union's window
+          vo_bucket_rank<BLOCK>(
+              [&](auto f) {
+#pragma unroll
+                for (int u = 0; u < kUnionPerThread; ++u)
+                  if ((sel >> u) & 1u) f(un.key[u], un.col(u));
+              },
+              prefix_edge(pf), kmax, static_cast<int>(kk), out_row.p, hist, comp, wtot, res);
+          return;  // (from this lambda: what follows stores the column order)
+        }
         uint32_t below[kGroups];
 #pragma unroll
         for (int q = 0; q < kGroups; ++q) {
@@ -1895,7 +1959,10 @@ topk_chunks_kernel(Params p) {
     }
     if (!done) __syncthreads();  // the streamed selection reuses the LDS
   }
-  if (!done) select_row_streamed<BLOCK>(row_ptr, L, p.k, out_row, hist, wtot, res);
+  if (!done) {
+    select_row_streamed<BLOCK>(row_ptr, L, p.k, out_row, hist, wtot, res);
+    if constexpr (VO) vo_rank_written<BLOCK>(row_ptr, L, p.k, out_row.p, comp);
+  }
   if (!exact_ok) {
     for (int c = 0; c < Gr; ++c) {
       const uint32_t cnt = coff[c + 1] - coff[c];
@@ -1928,13 +1995,14 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(uint4* p, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------
-// Value order: the selected columns of a row reordered by value (largest
-// first, equal values by ascending column).  One workgroup per row gathers
-// the m = min(k, L_i) selected values, forms the composite (key : reversed
-// column), whose descending order is the wanted one, and sorts the
-// composites of the row in LDS with a bitonic network; slots [m, k) keep -1.
+// Value order as a pass over an existing selection: the selected columns of
+// a row reordered by value (largest first, equal values by ascending
+// column).  One workgroup per row gathers the m = min(k, L_i) selected
+// values from the row and sorts their composites in LDS; slots [m, k) keep
+// -1.  The selection kernels rank in their own emission instead (VO); this
+// pass serves the cooperative split kernel and callers with an existing
+// selection.
 // ---------------------------------------------------------------------------
-constexpr int kSortMaxK = 4096;  // composites per row held in LDS (32 KB)
 
 template <int BLOCK>
 __global__ void __launch_bounds__(BLOCK) topk_value_order_kernel(const float* logits, int64_t row_stride,
@@ -1946,39 +2014,15 @@ __global__ void __launch_bounds__(BLOCK) topk_value_order_kernel(const float* lo
   L = L < 0 ? 0 : (L > row_stride ? row_stride : L);
   const int m = static_cast<int>(L < k ? L : k);
   if (m <= 1) return;
-  int n = 1;
-  while (n < m) n <<= 1;  // sorted size (power of two, at most kSortMaxK)
   const float* row_ptr = logits + row * row_stride;
   int32_t* out = idx + row * static_cast<int64_t>(k);
-  for (int i = threadIdx.x; i < n; i += BLOCK) {
-    uint64_t c = 0;  // padding sorts after every entry
-    if (i < m) {
-      const int32_t j = out[i];
-      // a column outside the row (not a selection's output) reads nothing
-      const bool ok = j >= 0 && j < L;
-      const uint32_t key = ok ? order_key(row_ptr[j]) : 0u;
-      c = (static_cast<uint64_t>(key) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(j));
-    }
-    comp[i] = c;
+  for (int i = threadIdx.x; i < m; i += BLOCK) {
+    const int32_t j = out[i];
+    // a column outside the row (not a selection's output) reads nothing
+    const bool ok = j >= 0 && j < L;
+    comp[i] = vo_composite(ok ? order_key(row_ptr[j]) : 0u, j);
   }
-  __syncthreads();
-  // bitonic network, descending: pairs (i, i + s) with bit s of i clear
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int s = size >> 1; s > 0; s >>= 1) {
-      for (int t = threadIdx.x; t < (n >> 1); t += BLOCK) {
-        const int i = ((t & ~(s - 1)) << 1) | (t & (s - 1));
-        const uint64_t a = comp[i], b = comp[i + s];
-        const bool first_desc = (i & size) == 0;  // this block of the network runs descending
-        if (first_desc ? a < b : a > b) {
-          comp[i] = b;
-          comp[i + s] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int i = threadIdx.x; i < m; i += BLOCK)
-    out[i] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(comp[i]));
+  vo_sort_store<BLOCK>(comp, m, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -2002,16 +2046,24 @@ struct KindInfo {
   Mode mode;     // one workgroup per row; cooperative split; chunked
   bool aligned;  // the kernel starts a row's span at the 16-byte boundary below it
   const void* fn;
+  const void* fn_vo;  // the same kernel writing value order (nullptr: a separate pass does)
 };
 
+#define MI_TOPK_KERNEL_PTR(...) reinterpret_cast<const void*>(&__VA_ARGS__)
 const KindInfo kKinds[kNumKinds] = {
-    {256, 16, kModeRow, true, reinterpret_cast<const void*>(&topk_row_kernel<256, 16>)},
-    {512, 16, kModeRow, true, reinterpret_cast<const void*>(&topk_row_kernel<512, 16>)},
-    {512, 32, kModeSplit, true, reinterpret_cast<const void*>(&topk_split_kernel<512, 32>)},
-    {512, 32, kModeRow, false, reinterpret_cast<const void*>(&topk_stream_kernel<512, 32>)},
-    {512, 64, kModeRow, false, reinterpret_cast<const void*>(&topk_stream_kernel<512, 64>)},
-    {512, 32, kModeChunks, false, reinterpret_cast<const void*>(&topk_chunks_kernel<512, 32>)},
+    {256, 16, kModeRow, true, MI_TOPK_KERNEL_PTR(topk_row_kernel<256, 16, false>),
+     MI_TOPK_KERNEL_PTR(topk_row_kernel<256, 16, true>)},
+    {512, 16, kModeRow, true, MI_TOPK_KERNEL_PTR(topk_row_kernel<512, 16, false>),
+     MI_TOPK_KERNEL_PTR(topk_row_kernel<512, 16, true>)},
+    {512, 32, kModeSplit, true, MI_TOPK_KERNEL_PTR(topk_split_kernel<512, 32>), nullptr},
+    {512, 32, kModeRow, false, MI_TOPK_KERNEL_PTR(topk_stream_kernel<512, 32, false>),
+     MI_TOPK_KERNEL_PTR(topk_stream_kernel<512, 32, true>)},
+    {512, 64, kModeRow, false, MI_TOPK_KERNEL_PTR(topk_stream_kernel<512, 64, false>),
+     MI_TOPK_KERNEL_PTR(topk_stream_kernel<512, 64, true>)},
+    {512, 32, kModeChunks, false, MI_TOPK_KERNEL_PTR(topk_chunks_kernel<512, 32, false>),
+     MI_TOPK_KERNEL_PTR(topk_chunks_kernel<512, 32, true>)},
 };
+#undef MI_TOPK_KERNEL_PTR
 
 struct DeviceInfo {
   int cus = 0;
@@ -2148,17 +2200,24 @@ size_t workspace_size_impl(int64_t num_rows, int64_t row_stride, int32_t k, int 
   return pl.ws_bytes;
 }
 
-int launch(const Plan& pl, Params prm, hipStream_t stream) {
+int value_order_launch(const Params& prm, hipStream_t stream);
+
+// vo: the output in value order, by the kernel's own value-order variant or,
+// for a kernel without one, by the value-order pass after it.
+int launch(const Plan& pl, Params prm, hipStream_t stream, bool vo = false) {
   const KindInfo& ki = kKinds[pl.kind];
   void* args[] = {&prm};
+  const void* fn = vo && ki.fn_vo != nullptr ? ki.fn_vo : ki.fn;
   hipError_t e;
   if (ki.mode == kModeSplit) {
-    e = hipLaunchCooperativeKernel(ki.fn, dim3(static_cast<unsigned>(pl.grid)), dim3(ki.block), args, 0,
+    e = hipLaunchCooperativeKernel(fn, dim3(static_cast<unsigned>(pl.grid)), dim3(ki.block), args, 0,
                                    stream);
   } else {
-    e = hipLaunchKernel(ki.fn, dim3(static_cast<unsigned>(pl.grid)), dim3(ki.block), args, 0, stream);
+    e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(pl.grid)), dim3(ki.block), args, 0, stream);
   }
-  return e == hipSuccess ? MI_TOPK_OK : MI_TOPK_ELAUNCH;
+  if (e != hipSuccess) return MI_TOPK_ELAUNCH;
+  if (vo && ki.fn_vo == nullptr) return value_order_launch(prm, stream);
+  return MI_TOPK_OK;
 }
 
 // Paged output: the page table, its row stride, page size and row-to-request
@@ -2172,9 +2231,10 @@ struct Paging {
 
 int topk_impl(const float* logits, int64_t row_stride, const int32_t* lengths, int64_t num_rows,
               int32_t k, int32_t* out, void* workspace, size_t workspace_bytes, int path, int chunks,
-              hipStream_t stream, const Paging& pg = Paging{}) {
+              hipStream_t stream, const Paging& pg = Paging{}, bool vo = false) {
   int st = check_shape(num_rows, row_stride, k);
   if (st != MI_TOPK_OK) return st;
+  if (vo && (k > kSortMaxK || pg.table != nullptr)) return MI_TOPK_EINVAL;
   if (path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_CHUNKS || chunks < 0) return MI_TOPK_EINVAL;
   if (num_rows == 0) return MI_TOPK_OK;
   if (!logits || !lengths || !out) return MI_TOPK_EINVAL;
@@ -2208,7 +2268,7 @@ int topk_impl(const float* logits, int64_t row_stride, const int32_t* lengths, i
   prm.row_req = pg.row_req;
   prm.page = pg.page;
   prm.page_log2 = (pg.page & (pg.page - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(pg.page)) : -1;
-  return launch(pl, prm, stream);
+  return launch(pl, prm, stream, vo);
 }
 
 }  // namespace
@@ -2327,15 +2387,45 @@ MI_TOPK_EXPORT const char* topk_status_string(int status) {
   }
 }
 
+namespace mitopk {
+namespace {
+int value_order_launch(const Params& prm, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_value_order_kernel<512>, dim3(static_cast<unsigned>(prm.num_rows)), dim3(512), 0,
+                     stream, prm.logits, prm.row_stride, prm.lengths, prm.k, prm.out);
+  return hipGetLastError() == hipSuccess ? MI_TOPK_OK : MI_TOPK_ELAUNCH;
+}
+}  // namespace
+}  // namespace mitopk
+
 MI_TOPK_EXPORT int topk_value_order(const float* logits, int64_t row_stride, const int32_t* lengths,
                                     int64_t num_rows, int32_t k, int32_t* idx, hipStream_t stream) {
   if (num_rows < 0 || num_rows > INT32_MAX || row_stride < 1 || k < 1 || k > kSortMaxK)
     return MI_TOPK_EINVAL;
   if (num_rows == 0) return MI_TOPK_OK;
   if (!logits || !lengths || !idx) return MI_TOPK_EINVAL;
-  hipLaunchKernelGGL(topk_value_order_kernel<512>, dim3(static_cast<unsigned>(num_rows)), dim3(512), 0, stream,
-                     logits, row_stride, lengths, k, idx);
-  return hipGetLastError() == hipSuccess ? MI_TOPK_OK : MI_TOPK_ELAUNCH;
+  Params prm{};
+  prm.logits = logits;
+  prm.row_stride = row_stride;
+  prm.lengths = lengths;
+  prm.num_rows = num_rows;
+  prm.k = k;
+  prm.out = idx;
+  return value_order_launch(prm, stream);
+}
+
+MI_TOPK_EXPORT int topk_indices_sorted_path(const float* logits, int64_t row_stride,
+                                            const int32_t* lengths, int64_t num_rows, int32_t k,
+                                            int32_t* out, void* workspace, size_t workspace_bytes,
+                                            int32_t path, int32_t chunks, hipStream_t stream) {
+  return topk_impl(logits, row_stride, lengths, num_rows, k, out, workspace, workspace_bytes, path,
+                   chunks, stream, Paging{}, true);
+}
+
+MI_TOPK_EXPORT int topk_indices_sorted(const float* logits, int64_t row_stride, const int32_t* lengths,
+                                       int64_t num_rows, int32_t k, int32_t* out, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  return topk_impl(logits, row_stride, lengths, num_rows, k, out, workspace, workspace_bytes,
+                   MI_TOPK_PATH_AUTO, 0, stream, Paging{}, true);
 }
 
 MI_TOPK_EXPORT int topk_debug_keys(const float* in, uint32_t* out, int64_t n, hipStream_t stream) {

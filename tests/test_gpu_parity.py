@@ -383,3 +383,35 @@ def test_value_order_rejects_bad_arguments():
         mt.topk_indices(logits, lens, 4097, order="value")
     with pytest.raises(ValueError):
         mt.topk_indices(logits, lens, 16, order="random")
+
+
+@pytest.mark.parametrize("path", ["local", "chunks", "split", "auto"])
+@pytest.mark.parametrize("kind", ["normal", "bf16", "levels", "equal", "ramp"])
+def test_value_order_every_path(path, kind):
+    # value order ranked inside each emission site: trivial rows (L <= k),
+    # rows held in registers, the streaming kernel's list and its exact
+    # fallback, the chunked merge, its streamed fallback and one-chunk rows;
+    # the cooperative split kernel is followed by the value-order pass
+    k = 1024
+    stride = 32768 if path == "local" else 131072
+    lengths = [stride, stride - 1, 1000, 5000, 8192, 9000, 16385, 3, 4095]
+    w = workloads.make_custom(len(lengths), stride, lengths, k, seed=len(kind) + stride, kind=kind)
+    logits, lens = device_view(w, offset=1 if path == "split" else 0)
+    out = torch.full((w.num_rows, k), SENTINEL, dtype=torch.int32, device="cuda:0")
+    mt.topk_indices(logits, lens, k, out=out, path=path, order="value")
+    torch.cuda.synchronize()
+    exp = oracle_topk(w.flat.numpy(), stride, w.lengths.numpy(), w.num_rows, k, order="value")
+    got = out.cpu().numpy()
+    bad = np.nonzero(np.any(got != exp, axis=1))[0]
+    assert bad.size == 0, f"{path} {kind}: rows {bad.tolist()} differ"
+
+
+def test_value_order_pass_on_an_existing_selection():
+    # topk_value_order: a separate pass that ranks an existing selection
+    w = workloads.make_custom(6, 50000, [50000, 20000, 100, 3000, 49999, 1], 2048, seed=4, kind="bf16")
+    logits, lens = device_view(w)
+    out = mt.topk_indices(logits, lens, 2048)
+    mt.value_order(logits, lens, out)
+    torch.cuda.synchronize()
+    exp = oracle_topk(w.flat.numpy(), 50000, w.lengths.numpy(), 6, 2048, order="value")
+    assert np.array_equal(out.cpu().numpy(), exp)
