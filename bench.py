@@ -1,7 +1,10 @@
 """Benchmark: batched, row-wise, stride-correct top-k index selection on one GPU.
 
 One step = one call of the library's top-k over the whole batch (all rows),
-with the inputs already resident in HBM.  Copies of the input are used in
+with the inputs already resident in HBM.  Before its W warm-up steps each
+timed workload runs its own launches untimed for 0.25 s (`clock_settle_s`):
+the GPU's clocks need about 10 ms of sustained load to leave their idle
+level, which a run of a few dozen launches would otherwise measure.  Copies of the input are used in
 turn, enough that more than 600 MB (twice the L2 caches plus the 256 MB
 last-level cache) is touched between two uses of one copy, so that no step
 finds its input in a cache (2 copies for the prefill batch, 21 for the
@@ -148,6 +151,24 @@ def gpu_env() -> dict:
 
 COLD_BYTES = 600e6   # bytes touched between two uses of one input copy
 MAX_COPIES = 64
+SETTLE_S = 0.25      # untimed load before the warm-up steps (clock settling)
+
+
+def settle(fn, seconds: float = SETTLE_S) -> int:
+    """Run `fn` back to back, untimed, for `seconds` of wall time.  After idling
+    the GPU's clocks are low and take about 10 ms of sustained load to reach
+    their working level (on MI355X, consecutive batches of 20 prefill launches
+    from idle measured 124, 117, 113, 110, 109, 109 us per launch, and again
+    116 us after 2 s idle), so every timed workload is preceded by this much
+    of its own work before its warm-up steps.  Returns the launches made."""
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+    return n
 
 
 def input_copies(w) -> int:
@@ -157,21 +178,29 @@ def input_copies(w) -> int:
 
 
 def time_workload(w, steps: int, warmup: int, copies: int = 2, paging: dict | None = None,
-                  order: str = "column"):
+                  order: str = "column", path: str = "auto"):
     import row_wise_top_topk_amd as mt
     dev = torch.device("cuda:0")
     pg = {} if paging is None else {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
                                     for k, v in paging.items()}
     if order != "column":
         pg["order"] = order
+    if path != "auto":
+        pg["path"] = path
     bufs = []
     for _ in range(copies):
         flat = w.flat.to(dev)
         bufs.append(flat.as_strided((w.num_rows, w.row_stride), (w.row_stride, 1)))
     lengths = w.lengths.to(dev)
     out = torch.empty((w.num_rows, w.k), dtype=torch.int32, device=dev)
-    need = mt.workspace_size(w.num_rows, w.row_stride, w.k)
+    need = mt.workspace_size(w.num_rows, w.row_stride, w.k, path=path)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev) if need else None
+    it = [0]
+
+    def one():
+        mt.topk_indices(bufs[it[0] % copies], lengths, w.k, out=out, workspace=ws, **pg)
+        it[0] += 1
+    settle(one)
     for i in range(warmup):
         mt.topk_indices(bufs[i % copies], lengths, w.k, out=out, workspace=ws, **pg)
     torch.cuda.synchronize()
@@ -228,6 +257,12 @@ def read_ceiling(w, steps: int, warmup: int, copies: int):
         f *= 2
     shape = (w.num_rows * f, w.row_stride // f)
     bufs = [w.flat.to(dev).as_strided(shape, (shape[1], 1)) for _ in range(copies)]
+    it = [0]
+
+    def one():
+        torch.amax(bufs[it[0] % copies], dim=1)
+        it[0] += 1
+    settle(one)
     for i in range(warmup):
         torch.amax(bufs[i % copies], dim=1)
     torch.cuda.synchronize()
@@ -315,6 +350,7 @@ def time_c128a(steps: int, warmup: int) -> dict:
             args = (ctypes.c_void_p(pos.data_ptr()), T, ratio, 0, None, None, 0, 2, None, 0, None,
                     ctypes.c_void_p(pbuf.data_ptr()), capacity, width, sp)
             fn = lib.c128a_topk_metadata
+            settle(lambda: fn(*args))
             for _ in range(warmup):
                 if fn(*args) != 0:
                     raise RuntimeError("c128a_topk_metadata failed")
@@ -365,6 +401,9 @@ def time_config(name: str, steps: int, warmup: int, with_read_ceiling: bool = Fa
            "achieved_gbs": b / (m * 1e-3) / 1e9,
            "frac": b / (m * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "traffic": measured_traffic(name)}
+    tp, _, _ = time_workload(w, steps, warmup, copies=c, path="persist")
+    res["persistent_grid"] = {"launch_us_mean": tp / steps * 1e3,
+                              "over_plain_us": (tp - t) / steps * 1e3}
     if with_read_ceiling:
         rc = read_ceiling(w, steps, warmup, c)
         res["read_ceiling"] = {"us_per_launch": rc["us_per_launch"], "gbs": rc["gbs"], "frac": rc["frac"],
@@ -450,6 +489,7 @@ def main() -> None:
                       "p50": float(np.percentile(per_launch, 50)) * 1e3,
                       "p90": float(np.percentile(per_launch, 90)) * 1e3},
         "host_wall_s": wall,
+        "clock_settle_s": SETTLE_S,
         "env": gpu_env(),
     }
     others = [n for n in args.others.split(",") if n and n != args.workload]
@@ -468,6 +508,11 @@ def main() -> None:
                                  "over_plain_us": (vo_ms / args.steps - avg_launch_ms) * 1e3,
                                  "note": "topk_indices(order='value'): the selection with each "
                                          "row's columns ranked by value"}
+        pers_ms, _, _ = time_workload(w, args.steps, args.warmup, copies=copies, path="persist")
+        result["persistent_grid"] = {"launch_us_mean": pers_ms / args.steps * 1e3,
+                                     "over_plain_us": (pers_ms / args.steps - avg_launch_ms) * 1e3,
+                                     "note": "path='persist': the same kernel on a fixed grid of the "
+                                             "workgroups the device holds at once"}
         warm_ms, _, _ = time_workload(w, args.steps, args.warmup, copies=1)
         result["warm_cache"] = {"input_copies": 1, "launch_us_mean": warm_ms / args.steps * 1e3,
                                 "achieved_gbs": alg_bytes / (warm_ms / args.steps * 1e-3) / 1e9,

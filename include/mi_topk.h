@@ -108,6 +108,16 @@ const char* topk_status_string(int status);
  *                       its own chunk, and the row's last workgroup selects
  *                       among them (an ordinary launch; k <= 4096, `chunks`
  *                       ignored).
+ *   MI_TOPK_PATH_PERSIST the kernel MI_TOPK_PATH_AUTO takes, launched on a
+ *                       fixed grid of as many workgroups as the device holds
+ *                       at once (compute units x the kernel's residency),
+ *                       whatever the batch: each workgroup loops over rows
+ *                       (or chunks).  The pages' serving paths pair such a
+ *                       persistent pool for large batches with a per-row
+ *                       cluster for small ones (vLLM PR #42169 report,
+ *                       实现拆解: persistent_topk; SGLang PR #34167 page,
+ *                       风险与影响 item 5: the persistent-pool path).  The
+ *                       cooperative split kernel is launched as usual.
  * topk_workspace_size_path() and topk_indices_path() otherwise behave like
  * topk_workspace_size() and topk_indices().
  */
@@ -115,6 +125,7 @@ const char* topk_status_string(int status);
 #define MI_TOPK_PATH_LOCAL 1
 #define MI_TOPK_PATH_SPLIT 2
 #define MI_TOPK_PATH_CHUNKS 3
+#define MI_TOPK_PATH_PERSIST 4
 
 size_t topk_workspace_size_path(int64_t num_rows, int64_t row_stride, int32_t k,
                                 int32_t path, int32_t chunks);
@@ -205,8 +216,11 @@ int topk_indices_sorted_path(const float* logits, int64_t row_stride, const int3
  * Describe the launch topk_indices_path() would make, without launching:
  * writes up to 7 int64 values to `info` (path, block threads, elements per
  * thread, chunk elements, chunks per row, grid workgroups, workspace bytes)
- * for a 16-byte-aligned `logits`.  Returns a status code.
+ * for a 16-byte-aligned `logits`.  The path is MI_TOPK_PATH_LOCAL, _SPLIT or
+ * _CHUNKS, with MI_TOPK_PLAN_PERSIST set for a fixed-grid launch.  Returns a
+ * status code.
  */
+#define MI_TOPK_PLAN_PERSIST 16
 int topk_plan_describe(int64_t num_rows, int64_t row_stride, int32_t k, int32_t path,
                        int32_t chunks, int64_t* info);
 
@@ -214,7 +228,8 @@ int topk_plan_describe(int64_t num_rows, int64_t row_stride, int32_t k, int32_t 
  * The same description for a device given by its properties instead of the
  * current one: `cus` compute units, `coop` nonzero if it supports cooperative
  * launches, `split_per_cu` co-resident workgroups of the cooperative split
- * kernel per compute unit.  Makes no HIP call (the host planning alone, e.g.
+ * kernel per compute unit (the fixed grids take the other kernels'
+ * residencies on gfx950).  Makes no HIP call (the host planning alone, e.g.
  * for tests on a machine without a GPU).  Returns a status code, as
  * topk_plan_describe() (MI_TOPK_EINVAL also for cus < 1 or split_per_cu < 0).
  */

@@ -15,14 +15,16 @@ import threading
 import torch
 
 __all__ = [
-    "PATH_AUTO", "PATH_LOCAL", "PATH_SPLIT", "PATH_CHUNKS",
+    "PATH_AUTO", "PATH_LOCAL", "PATH_SPLIT", "PATH_CHUNKS", "PATH_PERSIST", "PLAN_PERSIST",
     "library_path", "load_library", "topk_indices", "workspace_size",
     "plan_describe", "debug_keys", "workspace_error", "status_string",
     "c128a_active_width", "c128a_topk_metadata",
 ]
 
-PATH_AUTO, PATH_LOCAL, PATH_SPLIT, PATH_CHUNKS = 0, 1, 2, 3
-_PATHS = {"auto": PATH_AUTO, "local": PATH_LOCAL, "split": PATH_SPLIT, "chunks": PATH_CHUNKS}
+PATH_AUTO, PATH_LOCAL, PATH_SPLIT, PATH_CHUNKS, PATH_PERSIST = 0, 1, 2, 3, 4
+PLAN_PERSIST = 16   # set in plan_describe()["path"] for a fixed-grid launch
+_PATHS = {"auto": PATH_AUTO, "local": PATH_LOCAL, "split": PATH_SPLIT, "chunks": PATH_CHUNKS,
+          "persist": PATH_PERSIST}
 MAX_K = 1 << 24
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -585,11 +585,9 @@ __device__ __forceinline__ void select_row(uint32_t (&raw)[E], const Chunk& ch, 
 // VO: the selected columns leave ranked by value (their composites sorted in
 // LDS) instead of in ascending column order.
 template <int BLOCK, int E, bool VO>
-__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
-topk_row_kernel(Params p) {
+__device__ __forceinline__ void row_item(const Params& p, int64_t row) {
   __shared__ RowLds<BLOCK> lds;
   static_assert(sizeof(RowLds<BLOCK>) >= 8 * kSortMaxK, "composites of a row fit the LDS");
-  const int64_t row = blockIdx.x;
   const int L = row_length(p, row);
   const OutRow out_row = out_row_of(p, row);
   const float* row_ptr = p.logits + row * p.row_stride;
@@ -605,6 +603,22 @@ topk_row_kernel(Params p) {
   load_raw<BLOCK, E>(raw, ch);
   select_row<BLOCK, E>(raw, ch, L, p.k, out_row, lds);
   if constexpr (VO) vo_rank_written<BLOCK>(row_ptr, L, p.k, out_row.p, comp);
+}
+
+// One workgroup per row; PERSIST: a fixed grid whose workgroups take rows
+// blockIdx.x, blockIdx.x + gridDim.x, ... (the launch does not depend on the
+// batch).
+template <int BLOCK, int E, bool VO, bool PERSIST>
+__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+topk_row_kernel(Params p) {
+  if constexpr (PERSIST) {
+    for (int64_t row = blockIdx.x; row < p.num_rows; row += gridDim.x) {
+      row_item<BLOCK, E, VO>(p, row);
+      __syncthreads();  // the LDS is reused by the next row
+    }
+  } else {
+    row_item<BLOCK, E, VO>(p, blockIdx.x);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -816,15 +830,13 @@ __device__ __forceinline__ uint32_t filter_stream(const StreamGeom<BLOCK, NP>& g
 }
 
 template <int BLOCK, int NP, bool VO>
-__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(6)))
-topk_stream_kernel(Params p) {
+__device__ __forceinline__ void stream_item(const Params& p, int64_t row) {
   constexpr int NW = BLOCK / kWave;
   __shared__ StreamLds<BLOCK> lds;
   // composites of a row; their bucket ranking: bins, staging, scatter (16 KB each)
   static_assert(sizeof(lds.u) >= 8 * kSortMaxK && sizeof(lds.u) >= 12 * kFirstBins,
                 "composites of a row fit the LDS");
   uint64_t* comp = reinterpret_cast<uint64_t*>(lds.u.list);
-  const int64_t row = blockIdx.x;
   const int L = row_length(p, row);
   const OutRow out_row = out_row_of(p, row);
   const float* row_ptr = p.logits + row * p.row_stride;
@@ -996,6 +1008,19 @@ topk_stream_kernel(Params p) {
     } else {
       vo_rank_written<BLOCK>(row_ptr, L, p.k, out_row.p, comp);
     }
+  }
+}
+
+template <int BLOCK, int NP, bool VO, bool PERSIST>
+__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(6)))
+topk_stream_kernel(Params p) {
+  if constexpr (PERSIST) {
+    for (int64_t row = blockIdx.x; row < p.num_rows; row += gridDim.x) {
+      stream_item<BLOCK, NP, VO>(p, row);
+      __syncthreads();  // the LDS is reused by the next row
+    }
+  } else {
+    stream_item<BLOCK, NP, VO>(p, blockIdx.x);
   }
 }
 
@@ -1474,8 +1499,7 @@ __device__ __forceinline__ void hist_add_entries(uint32_t* hist, BinOf bin_of, T
 }
 
 template <int BLOCK, int E, bool VO>
-__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
-topk_chunks_kernel(Params p) {
+__device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
   constexpr int NW = BLOCK / kWave;
   // the histogram's words; with VO also the composites of the row (32 KB)
   // behind them
@@ -1489,8 +1513,8 @@ topk_chunks_kernel(Params p) {
   __shared__ uint32_t res[12];
   const int tid = threadIdx.x;
   const int G = p.G;
-  const int64_t row = blockIdx.x / G;
-  const int g = static_cast<int>(blockIdx.x % G);
+  const int64_t row = item / G;
+  const int g = static_cast<int>(item % G);
   const int L = row_length(p, row);
   const OutRow out_row = out_row_of(p, row);
   const float* row_ptr = p.logits + row * p.row_stride;
@@ -1981,6 +2005,23 @@ topk_chunks_kernel(Params p) {
   }
 }
 
+// One workgroup per chunk of a row; PERSIST: a fixed grid whose workgroups
+// take chunks blockIdx.x, blockIdx.x + gridDim.x, ... in (row, chunk)
+// order.  No workgroup ever waits for another, so any grid drains.
+template <int BLOCK, int E, bool VO, bool PERSIST>
+__global__ void __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+topk_chunks_kernel(Params p) {
+  if constexpr (PERSIST) {
+    const int64_t items = p.num_rows * p.G;
+    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+      chunks_item<BLOCK, E, VO>(p, item);
+      __syncthreads();  // the LDS is reused by the next chunk
+    }
+  } else {
+    chunks_item<BLOCK, E, VO>(p, blockIdx.x);
+  }
+}
+
 __global__ void debug_keys_kernel(const float* in, uint32_t* out, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) out[i] = order_key(in[i]);
@@ -2046,22 +2087,29 @@ struct KindInfo {
   Mode mode;     // one workgroup per row; cooperative split; chunked
   bool aligned;  // the kernel starts a row's span at the 16-byte boundary below it
   const void* fn;
-  const void* fn_vo;  // the same kernel writing value order (nullptr: a separate pass does)
+  const void* fn_vo;       // the same kernel writing value order (nullptr: a separate pass does)
+  const void* fn_persist;  // the same kernel on a fixed grid (nullptr: none)
+  int resident_per_cu;     // co-resident workgroups per CU on gfx950 (registers, LDS)
 };
 
 #define MI_TOPK_KERNEL_PTR(...) reinterpret_cast<const void*>(&__VA_ARGS__)
 const KindInfo kKinds[kNumKinds] = {
-    {256, 16, kModeRow, true, MI_TOPK_KERNEL_PTR(topk_row_kernel<256, 16, false>),
-     MI_TOPK_KERNEL_PTR(topk_row_kernel<256, 16, true>)},
-    {512, 16, kModeRow, true, MI_TOPK_KERNEL_PTR(topk_row_kernel<512, 16, false>),
-     MI_TOPK_KERNEL_PTR(topk_row_kernel<512, 16, true>)},
-    {512, 32, kModeSplit, true, MI_TOPK_KERNEL_PTR(topk_split_kernel<512, 32>), nullptr},
-    {512, 32, kModeRow, false, MI_TOPK_KERNEL_PTR(topk_stream_kernel<512, 32, false>),
-     MI_TOPK_KERNEL_PTR(topk_stream_kernel<512, 32, true>)},
-    {512, 64, kModeRow, false, MI_TOPK_KERNEL_PTR(topk_stream_kernel<512, 64, false>),
-     MI_TOPK_KERNEL_PTR(topk_stream_kernel<512, 64, true>)},
-    {512, 32, kModeChunks, false, MI_TOPK_KERNEL_PTR(topk_chunks_kernel<512, 32, false>),
-     MI_TOPK_KERNEL_PTR(topk_chunks_kernel<512, 32, true>)},
+    {256, 16, kModeRow, true, MI_TOPK_KERNEL_PTR(topk_row_kernel<256, 16, false, false>),
+     MI_TOPK_KERNEL_PTR(topk_row_kernel<256, 16, true, false>),
+     MI_TOPK_KERNEL_PTR(topk_row_kernel<256, 16, false, true>), 4},
+    {512, 16, kModeRow, true, MI_TOPK_KERNEL_PTR(topk_row_kernel<512, 16, false, false>),
+     MI_TOPK_KERNEL_PTR(topk_row_kernel<512, 16, true, false>),
+     MI_TOPK_KERNEL_PTR(topk_row_kernel<512, 16, false, true>), 2},
+    {512, 32, kModeSplit, true, MI_TOPK_KERNEL_PTR(topk_split_kernel<512, 32>), nullptr, nullptr, 2},
+    {512, 32, kModeRow, false, MI_TOPK_KERNEL_PTR(topk_stream_kernel<512, 32, false, false>),
+     MI_TOPK_KERNEL_PTR(topk_stream_kernel<512, 32, true, false>),
+     MI_TOPK_KERNEL_PTR(topk_stream_kernel<512, 32, false, true>), 3},
+    {512, 64, kModeRow, false, MI_TOPK_KERNEL_PTR(topk_stream_kernel<512, 64, false, false>),
+     MI_TOPK_KERNEL_PTR(topk_stream_kernel<512, 64, true, false>),
+     MI_TOPK_KERNEL_PTR(topk_stream_kernel<512, 64, false, true>), 3},
+    {512, 32, kModeChunks, false, MI_TOPK_KERNEL_PTR(topk_chunks_kernel<512, 32, false, false>),
+     MI_TOPK_KERNEL_PTR(topk_chunks_kernel<512, 32, true, false>),
+     MI_TOPK_KERNEL_PTR(topk_chunks_kernel<512, 32, false, true>), 2},
 };
 #undef MI_TOPK_KERNEL_PTR
 
@@ -2069,6 +2117,7 @@ struct DeviceInfo {
   int cus = 0;
   int coop = 0;
   int split_per_cu = 0;  // co-resident split workgroups per CU
+  int per_cu[kNumKinds] = {};  // co-resident workgroups per CU of each kernel on its fixed grid
   hipError_t status = hipSuccess;
 };
 
@@ -2089,6 +2138,10 @@ hipError_t device_info(DeviceInfo* out) {
     if (d.status == hipSuccess)
       d.status = hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.split_per_cu, kKinds[kSplit512x32].fn,
                                                               kKinds[kSplit512x32].block, 0);
+    for (int i = 0; i < kNumKinds && d.status == hipSuccess; ++i)
+      if (kKinds[i].fn_persist != nullptr)
+        d.status = hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.per_cu[i], kKinds[i].fn_persist,
+                                                                kKinds[i].block, 0);
 
     g_dev[dev] = d;
   });
@@ -2103,6 +2156,7 @@ struct Plan {
   int rows_per_iter = 0;
   int64_t grid = 0;
   size_t ws_bytes = 0;
+  bool persist = false;  // the kernel's fixed-grid form
 };
 
 int64_t cap_of(int kind) { return static_cast<int64_t>(kKinds[kind].block) * kKinds[kind].e; }
@@ -2115,8 +2169,28 @@ int64_t span_of(int kind, int64_t row_stride, int head_max) {
 
 // head_max: largest misalignment (in elements) of a row start below a 16-byte
 // boundary: 0 when logits is 16-byte aligned and row_stride % 4 == 0, else 3.
+int make_plan_kernel(int64_t num_rows, int64_t row_stride, int32_t k, int path, int chunks, int head_max,
+                     const DeviceInfo& dev, Plan* pl);
+
+// MI_TOPK_PATH_PERSIST: the kernel the automatic choice takes, on a fixed
+// grid of the workgroups the device holds at once (its compute units times
+// the kernel's residency), whatever the batch; the cooperative split kernel
+// already runs on a grid of co-resident workgroups.
 int make_plan(int64_t num_rows, int64_t row_stride, int32_t k, int path, int chunks, int head_max,
               const DeviceInfo& dev, Plan* pl) {
+  const bool persist = path == MI_TOPK_PATH_PERSIST;
+  const int st = make_plan_kernel(num_rows, row_stride, k, persist ? MI_TOPK_PATH_AUTO : path, chunks,
+                                  head_max, dev, pl);
+  if (st != MI_TOPK_OK || !persist || kKinds[pl->kind].fn_persist == nullptr) return st;
+  const int per_cu = dev.per_cu[pl->kind];
+  if (per_cu < 1) return MI_TOPK_ELAUNCH;
+  pl->persist = true;
+  pl->grid = static_cast<int64_t>(per_cu) * dev.cus;
+  return MI_TOPK_OK;
+}
+
+int make_plan_kernel(int64_t num_rows, int64_t row_stride, int32_t k, int path, int chunks, int head_max,
+                     const DeviceInfo& dev, Plan* pl) {
   const int64_t need = row_stride + head_max;  // elements a row can span from its aligned start
   const bool fits_local = span_of(kLargestLocal, row_stride, head_max) <= cap_of(kLargestLocal);
   bool split;
@@ -2207,7 +2281,8 @@ int value_order_launch(const Params& prm, hipStream_t stream);
 int launch(const Plan& pl, Params prm, hipStream_t stream, bool vo = false) {
   const KindInfo& ki = kKinds[pl.kind];
   void* args[] = {&prm};
-  const void* fn = vo && ki.fn_vo != nullptr ? ki.fn_vo : ki.fn;
+  const bool vo_pass = vo && (ki.fn_vo == nullptr || pl.persist);  // value order by the separate pass
+  const void* fn = pl.persist ? ki.fn_persist : (vo && !vo_pass ? ki.fn_vo : ki.fn);
   hipError_t e;
   if (ki.mode == kModeSplit) {
     e = hipLaunchCooperativeKernel(fn, dim3(static_cast<unsigned>(pl.grid)), dim3(ki.block), args, 0,
@@ -2216,7 +2291,7 @@ int launch(const Plan& pl, Params prm, hipStream_t stream, bool vo = false) {
     e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(pl.grid)), dim3(ki.block), args, 0, stream);
   }
   if (e != hipSuccess) return MI_TOPK_ELAUNCH;
-  if (vo && ki.fn_vo == nullptr) return value_order_launch(prm, stream);
+  if (vo_pass) return value_order_launch(prm, stream);
   return MI_TOPK_OK;
 }
 
@@ -2235,7 +2310,7 @@ int topk_impl(const float* logits, int64_t row_stride, const int32_t* lengths, i
   int st = check_shape(num_rows, row_stride, k);
   if (st != MI_TOPK_OK) return st;
   if (vo && (k > kSortMaxK || pg.table != nullptr)) return MI_TOPK_EINVAL;
-  if (path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_CHUNKS || chunks < 0) return MI_TOPK_EINVAL;
+  if (path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_PERSIST || chunks < 0) return MI_TOPK_EINVAL;
   if (num_rows == 0) return MI_TOPK_OK;
   if (!logits || !lengths || !out) return MI_TOPK_EINVAL;
   if ((reinterpret_cast<uintptr_t>(logits) & 3u) || (reinterpret_cast<uintptr_t>(lengths) & 3u) ||
@@ -2282,7 +2357,7 @@ MI_TOPK_EXPORT size_t topk_workspace_size(int64_t num_rows, int64_t row_stride, 
 
 MI_TOPK_EXPORT size_t topk_workspace_size_path(int64_t num_rows, int64_t row_stride, int32_t k,
                                                int32_t path, int32_t chunks) {
-  if (path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_CHUNKS || chunks < 0) return 0;
+  if (path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_PERSIST || chunks < 0) return 0;
   return workspace_size_impl(num_rows, row_stride, k, path, chunks);
 }
 
@@ -2339,6 +2414,7 @@ int describe(int64_t num_rows, int64_t row_stride, int32_t k, int32_t path, int3
   info[0] = ki.mode == kModeSplit ? MI_TOPK_PATH_SPLIT
             : ki.mode == kModeChunks ? MI_TOPK_PATH_CHUNKS
                                      : MI_TOPK_PATH_LOCAL;
+  if (pl.persist) info[0] |= MI_TOPK_PLAN_PERSIST;
   info[1] = ki.block;
   info[2] = ki.e;
   info[3] = pl.chunk;
@@ -2354,7 +2430,7 @@ MI_TOPK_EXPORT int topk_plan_describe(int64_t num_rows, int64_t row_stride, int3
                                       int32_t chunks, int64_t* info) {
   const int st = check_shape(num_rows, row_stride, k);
   if (st != MI_TOPK_OK) return st;
-  if (!info || path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_CHUNKS || chunks < 0) return MI_TOPK_EINVAL;
+  if (!info || path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_PERSIST || chunks < 0) return MI_TOPK_EINVAL;
   DeviceInfo dev;
   if (device_info(&dev) != hipSuccess) return MI_TOPK_ELAUNCH;
   return describe(num_rows, row_stride, k, path, chunks, dev, info);
@@ -2365,13 +2441,14 @@ MI_TOPK_EXPORT int topk_plan_describe_for(int64_t num_rows, int64_t row_stride, 
                                           int32_t split_per_cu, int64_t* info) {
   const int st = check_shape(num_rows, row_stride, k);
   if (st != MI_TOPK_OK) return st;
-  if (!info || path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_CHUNKS || chunks < 0 || cus < 1 ||
+  if (!info || path < MI_TOPK_PATH_AUTO || path > MI_TOPK_PATH_PERSIST || chunks < 0 || cus < 1 ||
       split_per_cu < 0)
     return MI_TOPK_EINVAL;
   DeviceInfo dev;
   dev.cus = cus;
   dev.coop = coop;
   dev.split_per_cu = split_per_cu;
+  for (int i = 0; i < kNumKinds; ++i) dev.per_cu[i] = kKinds[i].resident_per_cu;
   return describe(num_rows, row_stride, k, path, chunks, dev, info);
 }
 

@@ -415,3 +415,42 @@ def test_value_order_pass_on_an_existing_selection():
     torch.cuda.synchronize()
     exp = oracle_topk(w.flat.numpy(), 50000, w.lengths.numpy(), 6, 2048, order="value")
     assert np.array_equal(out.cpu().numpy(), exp)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "long", "prefill", "adversarial"])
+def test_persistent_grid_matches_oracle(name):
+    # the kernels on their fixed grids: workgroups loop over rows or chunks
+    w = workloads.make(name)
+    got = run_gpu(w, path="persist")
+    assert_parity(w, got, label=f"persist {name}")
+
+
+def test_persistent_grid_residency_matches_the_host_table():
+    # the fixed grid the device reports equals the one host planning derives
+    # from the kernels' gfx950 residency (the table topk_plan_describe_for uses)
+    import torch as _t
+    cus = _t.cuda.get_device_properties(0).multi_processor_count
+    for shape in ((4096, 32768, 2048), (4, 4096, 512), (4096, 6000, 64), (8, 900096, 2048)):
+        dev = mt.plan_describe(*shape, path="persist")
+        host = mt.plan_describe_for(*shape, path="persist", cus=cus)
+        assert dev == host, (shape, dev, host)
+
+
+def test_persistent_grid_random_shapes_and_value_order():
+    rng = np.random.default_rng(77)
+    for trial in range(40):
+        rows = int(rng.integers(1, 700))
+        stride = int(rng.integers(100, 40000)) if rows > 64 else int(rng.integers(100, 300000))
+        stride = min(stride, 3_000_000 // rows)     # keeps the oracle fast
+        k = int(rng.integers(1, 2049))
+        lengths = rng.integers(0, stride + 1, size=rows)
+        w = workloads.make_custom(rows, stride, lengths, k, seed=500 + trial,
+                                  kind=["normal", "bf16", "levels"][trial % 3])
+        got = run_gpu(w, path="persist")
+        assert_parity(w, got, label=f"persist trial {trial} rows={rows} stride={stride} k={k}")
+    w = workloads.make_custom(600, 9000, [9000, 8000, 100, 4097] * 150, 1024, seed=9, kind="bf16")
+    logits, lens = device_view(w)
+    out = mt.topk_indices(logits, lens, 1024, path="persist", order="value")
+    torch.cuda.synchronize()
+    exp = oracle_topk(w.flat.numpy(), 9000, w.lengths.numpy(), 600, 1024, order="value")
+    assert np.array_equal(out.cpu().numpy(), exp)

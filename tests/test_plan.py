@@ -77,3 +77,28 @@ def test_forced_paths_and_limits():
     with pytest.raises(RuntimeError, match="status 1"):      # no compute units
         mt.plan_describe_for(8, 900096, 2048, cus=0)
     assert mt.plan_describe_for(1, 1024 * 16384, 16, path="chunks")["chunks_per_row"] == 1024
+
+
+@pytest.mark.parametrize("shape,path,grid", [
+    ((4096, 32768, 2048), mt.PATH_LOCAL, 3 * 256),   # streaming kernel: 3 workgroups per CU
+    ((4, 4096, 512), mt.PATH_LOCAL, 4 * 256),        # register kernel 256 x 16: 4 per CU
+    ((4096, 6000, 64), mt.PATH_LOCAL, 2 * 256),      # register kernel 512 x 16: 2 per CU
+    ((8, 900096, 2048), mt.PATH_CHUNKS, 2 * 256),    # chunked kernel: 2 per CU
+    ((256, 131072, 1024), mt.PATH_CHUNKS, 2 * 256),
+])
+def test_persistent_grid_is_fixed_by_the_device(shape, path, grid):
+    # the fixed grid: the device's compute units times the kernel's residency,
+    # whatever the batch; the kernel is the automatic choice
+    d = mt.plan_describe_for(*shape, path="persist")
+    assert d["path"] == path | mt.PLAN_PERSIST
+    assert d["grid"] == grid
+    auto = mt.plan_describe_for(*shape)
+    assert (d["block"], d["elems_per_thread"], d["chunks_per_row"], d["workspace_bytes"]) == (
+        auto["block"], auto["elems_per_thread"], auto["chunks_per_row"], auto["workspace_bytes"])
+    half = mt.plan_describe_for(max(1, shape[0] // 2), shape[1], shape[2], path="persist")
+    assert half["grid"] == grid
+
+
+def test_persistent_path_keeps_the_cooperative_split_launch():
+    d = mt.plan_describe_for(8, 900096, 4097, path="persist")
+    assert d["path"] == mt.PATH_SPLIT and d["grid"] == 512
