@@ -39,13 +39,13 @@ constexpr int kMaxRounds = 7;
 // value.  -0.0 (0x80000000) maps to 0x80000000, the key of +0.0, so the two
 // zeros tie as IEEE says they do.  No value maps to 0 (the smallest image is
 // 1, from the all-ones NaN pattern); key 0 marks entries outside the row.
-__device__ __forceinline__ uint32_t order_key(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (static_cast<int32_t>(u) >= 0) ? (u | 0x80000000u) : (0u - u);
-}
+// Written without a compare and select: with s = all sign bits (0 or ~0),
+// (u ^ (s | 2^31)) - s is u | 2^31 for s = 0 and ~u + 1 = -u for s = ~0.
 __device__ __forceinline__ uint32_t order_key_bits(uint32_t u) {
-  return (static_cast<int32_t>(u) >= 0) ? (u | 0x80000000u) : (0u - u);
+  const uint32_t s = static_cast<uint32_t>(static_cast<int32_t>(u) >> 31);
+  return (u ^ (s | 0x80000000u)) - s;
 }
+__device__ __forceinline__ uint32_t order_key(float x) { return order_key_bits(__float_as_uint(x)); }
 
 // A fixed prefix of the composite (key : reversed index).
 //   bits <= 32: kp holds the top `bits` bits of the key;

@@ -643,7 +643,7 @@ topk_row_kernel(Params p) {
 // memory (or, for a row of at most 16 positions per thread, from registers).
 // ---------------------------------------------------------------------------
 constexpr int kChunkPos = 16;     // positions per chunk, per thread
-constexpr int kStreamBufs = 3;    // chunks in flight per wavefront
+constexpr int kStreamBufs = 2;    // chunks in flight per wavefront
 constexpr int kStreamRegion = 768;  // list entries per wavefront
 
 // List entry i of wavefront w: raw bits at list[w*kStreamRegion + i], column
@@ -1583,22 +1583,35 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
   uint8_t* ckeys = rb + 256 + ((12 * static_cast<size_t>(G) + 255) / 256) * 256;  // u32 [G][kChunkCap]
   uint8_t* ccols = ckeys + static_cast<size_t>(G) * kChunkCap * 4;                 // u16 [G][kChunkCap]
 
-  // sample: the first kChunkSamples positions of each thread
+  // sample: the first kChunkSamples positions of each thread, ns entries
+  // (the first 64*kChunkSamples elements of each wavefront's stretch that
+  // lie inside the chunk); the bound is the nd-th largest of them.
+  int ns = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) ns += min(max(clen - v * kWave * E, 0), kWave * kChunkSamples);
+  const uint32_t nd = static_cast<uint32_t>((3ull * kk * ns + 2ull * L - 1) / (2ull * L)) + 16u;
+  // When nd is small against the 512 threads, each thread contributes only
+  // the largest of its samples: the nd largest samples then lie in nearly
+  // nd different threads, so the nd-th largest maximum is a bound just below
+  // the nd-th largest sample (never above it: the maxima are samples), found
+  // from 512 entries instead of 8192.  On smooth data the samples crowd into
+  // few first-digit bins, whose LDS atomics then serialise.
+  const bool by_max = nd <= 64u;
+  uint32_t smax = 0;
+#pragma unroll
+  for (int u = 0; u < kChunkSamples; ++u) smax = max(smax, kv[u]);  // positions past the row: key 1
   for (int i = tid; i < kFirstBins; i += BLOCK) hist[i] = 0;
   if (tid == 0) res[0] = 0u;
   __syncthreads();
-  hist_add_entries<kChunkSamples>(
-      hist, [&](int q) { return kv[q] >> (32 - kFirstBits); },
-      [&](int q) { return kv[q] > 1u; });  // positions past the row: key 1
+  if (by_max) {
+    if (smax > 1u) atomicAdd(&hist[smax >> (32 - kFirstBits)], 1u);
+  } else {
+    hist_add_entries<kChunkSamples>(
+        hist, [&](int q) { return kv[q] >> (32 - kFirstBits); },
+        [&](int q) { return kv[q] > 1u; });
+  }
   __syncthreads();
-  find_bucket_block<BLOCK, kFirstBins>(
-      hist,
-      [&](uint32_t ns) {
-        const uint32_t nd = static_cast<uint32_t>((3ull * kk * ns + 2ull * L - 1) / (2ull * L)) + 16u;
-        if (tid == 0) res[9] = nd;
-        return nd;
-      },
-      res, wtot);
+  find_bucket_block<BLOCK, kFirstBins>(hist, [nd](uint32_t) { return nd; }, res, wtot);
   __syncthreads();
   // The first-digit bin holding the need-th sample is refined by the next
   // digit, so the bound sits at that sample (to 22 bits) rather than at the
@@ -1607,20 +1620,41 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
   uint32_t lb = 2u;
   const uint32_t b0 = res[0];
   if (b0 != 0u) {
-    const uint32_t need2 = res[9] - res[1];
+    const uint32_t need2 = nd - res[1];
     __syncthreads();  // res and hist are reused
     for (int i = tid; i < kNextBins; i += BLOCK) hist[i] = 0;
     __syncthreads();
-    hist_add_entries<kChunkSamples>(
-        hist, [&](int q) { return (kv[q] >> (32 - kFirstBits - kNextBits)) & (kNextBins - 1); },
-        [&](int q) { return (kv[q] >> (32 - kFirstBits)) == b0; });
+    if (by_max) {
+      if ((smax >> (32 - kFirstBits)) == b0)
+        atomicAdd(&hist[(smax >> (32 - kFirstBits - kNextBits)) & (kNextBins - 1)], 1u);
+    } else {
+      hist_add_entries<kChunkSamples>(
+          hist, [&](int q) { return (kv[q] >> (32 - kFirstBits - kNextBits)) & (kNextBins - 1); },
+          [&](int q) { return (kv[q] >> (32 - kFirstBits)) == b0; });
+    }
     __syncthreads();
     find_bucket_block<BLOCK, kNextBins>(hist, [need2](uint32_t) { return need2; }, res, wtot);
     __syncthreads();
     lb = (b0 << (32 - kFirstBits)) | (res[0] << (32 - kFirstBits - kNextBits));
   }
 
-  to_keys(std::integral_constant<int, kChunkSamples>{}, std::integral_constant<int, E>{});
+  // The second half stays raw bits and is tested against the bound on them
+  // (key >= lb: for lb <= 2^31 the bits, unsigned, are <= 2^32 - lb; above
+  // that the bits, signed, are >= lb's low 31 bits); a key is formed only at
+  // positions where some lane passes.  Positions past the row read as
+  // kOutsideBits, whose key (1) is below every bound.
+  if (!whole) {
+#pragma unroll
+    for (int u = kChunkSamples; u < E; ++u) kv[u] = e0 + u * kWave < clen ? kv[u] : kOutsideBits;
+  }
+  const uint32_t ulim = 0u - lb;
+  const int32_t slim = static_cast<int32_t>(lb & 0x7FFFFFFFu);
+  const bool pos_bound = lb > 0x80000000u;
+  auto hit_of = [&](int u) -> bool {
+    if (u < kChunkSamples) return kv[u] >= lb;
+    return pos_bound ? static_cast<int32_t>(kv[u]) >= slim : kv[u] <= ulim;
+  };
+  auto key_of = [&](int u) -> uint32_t { return u < kChunkSamples ? kv[u] : order_key_bits(kv[u]); };
 
   // Publish the chunk's entries with key >= lb, in column order.  Each
   // wavefront stages its candidates in its own region of kWaveStage LDS
@@ -1637,17 +1671,18 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
   uint32_t cm = 0;   // the largest key of this thread's candidates
 #pragma unroll
   for (int u = 0; u < E; ++u) {
-    const bool hit = kv[u] >= lb;
+    const bool hit = hit_of(u);
     const uint64_t m = __ballot(hit);
     if (m != 0u) {  // most positions of a wavefront have no candidate
-      cm = hit ? max(cm, kv[u]) : cm;
+      const uint32_t key = key_of(u);
+      cm = hit ? max(cm, key) : cm;
       const uint32_t at = pos + lanes_below(m);
       if (hit && at < kWaveStage) {
-        hist[wv * kWaveStage + at] = kv[u];
+        hist[wv * kWaveStage + at] = key;
         scol[wv * kWaveStage + at] = static_cast<uint16_t>(e0 + u * kWave);
       }
       pos += static_cast<uint32_t>(__popcll(m));
-      tw += static_cast<uint32_t>(__popcll(__ballot(kv[u] == lb)));
+      tw += static_cast<uint32_t>(__popcll(__ballot(key == lb)));
     }
   }
   cm = wave_max(cm);
@@ -1720,14 +1755,15 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
       uint32_t at = my_kp, tr = my_tp;
 #pragma unroll
       for (int u = 0; u < E; ++u) {
-        const bool tie = kv[u] == lb;
+        const uint32_t key = key_of(u);
+        const bool tie = key == lb;
         const uint64_t mt = __ballot(tie);
-        const bool keep = kv[u] >= lb && (!tie || tr + lanes_below(mt) < limit);
+        const bool keep = key >= lb && (!tie || tr + lanes_below(mt) < limit);
         const uint64_t mk = __ballot(keep);
         if (mk != 0u) {
           const uint32_t a2 = at + lanes_below(mk);
           if (keep) {
-            hist[a2] = kv[u];
+            hist[a2] = key;
             scol[a2] = static_cast<uint16_t>(e0 + u * kWave);
           }
           at += static_cast<uint32_t>(__popcll(mk));
@@ -1843,6 +1879,12 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
     }
   }
   __syncthreads();
+  // the counts, bounds and largest keys have been read (into coff and res)
+  for (int c = tid; c < Gr; c += BLOCK) {
+    g_store(&counts[c], 0u);
+    g_store(&bounds[c], 0u);
+    g_store(&kmaxs[c], 0u);
+  }
   const uint32_t utotal = res[5], min_lb = res[6], max_lb = res[7];
   const bool fits = res[8] == 0u && utotal >= kk;
   const bool slotted = fits && res[10] <= 4u * Wg;
@@ -1885,6 +1927,20 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
     // the keys are consumed before the packed layout's column loads go
     // out, so no wait for those loads comes before the emission needs them
     asm volatile("" : : "v"(nz) : "memory");
+    if (slotted) {
+      // every slot of the union has been read (keys here, column offsets
+      // once they have arrived): return them to zero now, so that the stores
+      // drain during the rounds rather than after the output
+      uint32_t oz = 0;
+#pragma unroll
+      for (int q = 0; q < kGroups; ++q) oz |= un.offw[q].x | un.offw[q].y;
+      asm volatile("" : : "v"(oz) : "memory");
+#pragma unroll
+      for (int q = 0; q < kGroups; ++q) {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, krs, gslot[q] * 4, 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, crs, gslot[q] * 2, 0, kCoherent);
+      }
+    }
     if (!slotted) {
       uint32_t o[kUnionPerThread];
 #pragma unroll
@@ -1966,14 +2022,9 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
       });
     }
     done = edge >= max_lb;
-    // the slots read return to zero (other paths may use the workspace next)
-    if (slotted) {
-#pragma unroll
-      for (int q = 0; q < kGroups; ++q) {
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, krs, gslot[q] * 4, 0, kCoherent);
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, crs, gslot[q] * 2, 0, kCoherent);
-      }
-    } else {
+    // the slots read return to zero (other paths may use the workspace next;
+    // the slotted union's were cleared as soon as they were read)
+    if (!slotted) {
 #pragma unroll
       for (int u = 0; u < kUnionPerThread; ++u)
         if (un.key[u] != 0u) {
@@ -1997,11 +2048,6 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
         __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(0), crs, at * 2, 0, kCoherent);
       }
     }
-  }
-  for (int c = tid; c < Gr; c += BLOCK) {
-    g_store(&counts[c], 0u);
-    g_store(&bounds[c], 0u);
-    g_store(&kmaxs[c], 0u);
   }
 }
 
