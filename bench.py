@@ -154,13 +154,14 @@ MAX_COPIES = 64
 SETTLE_S = 0.25      # untimed load before the warm-up steps (clock settling)
 
 
-def settle(fn, seconds: float = SETTLE_S) -> int:
+def settle(fn, seconds: float | None = None) -> int:
     """Run `fn` back to back, untimed, for `seconds` of wall time.  After idling
     the GPU's clocks are low and take about 10 ms of sustained load to reach
     their working level (on MI355X, consecutive batches of 20 prefill launches
     from idle measured 124, 117, 113, 110, 109, 109 us per launch, and again
     116 us after 2 s idle), so every timed workload is preceded by this much
     of its own work before its warm-up steps.  Returns the launches made."""
+    seconds = SETTLE_S if seconds is None else seconds
     n = 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
@@ -412,6 +413,7 @@ def time_config(name: str, steps: int, warmup: int, with_read_ceiling: bool = Fa
 
 
 def main() -> None:
+    global SETTLE_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -430,7 +432,10 @@ def main() -> None:
                     help="only time the workload at several row counts and fit time against rows")
     ap.add_argument("--c128a-only", action="store_true",
                     help="only time the C128A metadata kernel at the page's shapes")
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="untimed load before each workload's warm-up (clock settling)")
     args = ap.parse_args()
+    SETTLE_S = args.settle_s
     if args.calibrate_copy:
         calibrate_copy()
         return
