@@ -1307,6 +1307,37 @@ struct UnionList {
 // A whole row read from memory in blocks of BLOCK*16 entries (position u of
 // thread (w, l) in block b is entry b*BLOCK*16 + w*1024 + u*64 + l, so the
 // visiting order is column order); entries past the row carry key 0.
+// Adds n to hist[bin] for each lane with n != 0 (n the same on all such
+// lanes): one atomic when those lanes share a bin.
+__device__ __forceinline__ void hist_add_lanes(uint32_t* hist, uint32_t bin, uint32_t n) {
+  const uint64_t tm = __ballot(n != 0u);
+  if (tm == 0u) return;
+  const int first = __ffsll(static_cast<unsigned long long>(tm)) - 1;
+  const uint32_t b0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), first));
+  if (__ballot(n != 0u && bin != b0) == 0u) {
+    if (static_cast<int>(__lane_id()) == first) atomicAdd(&hist[b0], n * static_cast<uint32_t>(__popcll(tm)));
+  } else if (n != 0u) {
+    atomicAdd(&hist[bin], n);
+  }
+}
+
+// Smallest and largest of a lane's keys of a block.
+__device__ __forceinline__ void lane_range(const uint32_t (&buf)[kChunkPos], uint32_t& mn, uint32_t& mx) {
+  mn = buf[0];
+  mx = buf[0];
+#pragma unroll
+  for (int u = 1; u < kChunkPos; ++u) {
+    mn = min(mn, buf[u]);
+    mx = max(mx, buf[u]);
+  }
+}
+
+// One workgroup streaming a row of L entries in blocks of BLOCK x kChunkPos:
+// wavefront w's part of a block is kChunkPos positions of 64 consecutive
+// columns, so a block's column order is (wavefront, position, lane).  A
+// pass over the row costs one CU's vector issue rate per operation on each
+// entry, so the passes below summarise each lane's 16 keys by their range
+// and do per-entry work only where the range leaves the answer open.
 template <int BLOCK>
 struct RowStream {
   __amdgpu_buffer_rsrc_t rsrc;
@@ -1330,74 +1361,163 @@ struct RowStream {
     for (int u = 0; u < kChunkPos; ++u)
       buf[u] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (e0 + u * kWave) * 4, 0, 0);
   }
-  __device__ __forceinline__ void keys(uint32_t (&buf)[kChunkPos], int e0) const {
+  // The block's keys; positions past the row get key 0, below every real
+  // key (which is at least 1).  full: the block lies inside the row.
+  __device__ __forceinline__ void keys(uint32_t (&buf)[kChunkPos], int e0, bool full) const {
+    if (full) {
 #pragma unroll
-    for (int u = 0; u < kChunkPos; ++u)
-      buf[u] = e0 + u * kWave < L ? order_key_bits(buf[u]) : 0u;
+      for (int u = 0; u < kChunkPos; ++u) buf[u] = order_key_bits(buf[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kChunkPos; ++u) buf[u] = e0 + u * kWave < L ? order_key_bits(buf[u]) : 0u;
+    }
   }
   // Visits the row's blocks in order, block b+kRowBufs-1 loading while
-  // block b is visited: visit(buf, e0) gets a block's keys.  The loads are
-  // issued unconditionally (past the row they read nothing), so the
-  // compiler's waits stay exact.
+  // block b is visited: visit(buf, e0, full) gets a block's keys and returns
+  // whether to go on (the same answer on every thread of the workgroup; the
+  // blocks after a false are skipped).  The loads are issued
+  // unconditionally (past the row they read nothing), so the compiler's
+  // waits stay exact.
   template <class V>
   __device__ __forceinline__ void blocks(V visit) const {
     uint32_t buf[kRowBufs][kChunkPos];
 #pragma unroll
     for (int i = 0; i < kRowBufs - 1; ++i) load(buf[i], elem0(i * kBlockElems));
+    bool go = true;
 #pragma unroll 1
-    for (int base = 0; base < L; base += kRowBufs * kBlockElems) {
+    for (int base = 0; go && base < L; base += kRowBufs * kBlockElems) {
 #pragma unroll
       for (int i = 0; i < kRowBufs; ++i) {
         const int bb = base + i * kBlockElems;
         load(buf[(i + kRowBufs - 1) % kRowBufs], elem0(bb + (kRowBufs - 1) * kBlockElems));
         const int e0 = elem0(bb);
-        keys(buf[i], e0);
-        visit(buf[i], e0);
+        const bool full = bb + kBlockElems <= L;
+        keys(buf[i], e0, full);
+        if (go) go = visit(buf[i], e0, full);
       }
     }
   }
-  template <class F>
-  __device__ __forceinline__ void operator()(F f) const {
-    blocks([&](const uint32_t (&buf)[kChunkPos], int e0) {
+  // Histogram of key digit d below the key prefix p (p.bits < 32; 0: every
+  // entry of the row).  A wavefront whose lanes each have their 16 keys
+  // outside the prefix or in one bin adds per lane (one atomic when the
+  // lanes share the bin); other blocks add entry by entry, aggregated per
+  // position (hist_add_wave).  With `tally`, also the row's keys above x
+  // and equal to x, added to gt_eq[0] and gt_eq[1] (x >= 1).
+  __device__ __forceinline__ void count(const Prefix& p, int d, uint32_t* hist, bool tally,
+                                        uint32_t x, uint32_t* gt_eq) const {
+    const int sh = 32 - p.bits;  // bits below the prefix
+    const uint32_t plo = p.bits == 0 ? 1u : max(p.kp << sh, 1u);
+    const uint32_t phi = p.bits == 0 ? 0xFFFFFFFFu : (p.kp << sh) | ((1u << sh) - 1u);
+    const uint32_t span = phi - plo;
+    const int dsh = sh - d;
+    const uint32_t dmask = (1u << d) - 1u;
+    auto bin = [&](uint32_t key) { return (key >> dsh) & dmask; };
+    auto take = [&](uint32_t key) { return key - plo <= span; };
+    uint32_t gt = 0, eq = 0;
+    blocks([&](const uint32_t (&buf)[kChunkPos], int, bool full) {
+      if (full) {
+        uint32_t mn, mx;
+        lane_range(buf, mn, mx);
+        if (tally) {
+          gt += mn > x ? static_cast<uint32_t>(kChunkPos) : 0u;
+          eq += mn == mx && mn == x ? static_cast<uint32_t>(kChunkPos) : 0u;
+          if (!(mn > x || mx < x || mn == mx)) {
 #pragma unroll
-      for (int u = 0; u < kChunkPos; ++u) f(buf[u], e0 + u * kWave);
+            for (int u = 0; u < kChunkPos; ++u) {
+              gt += buf[u] > x ? 1u : 0u;
+              eq += buf[u] == x ? 1u : 0u;
+            }
+          }
+        }
+        const bool none = mx < plo || mn > phi;
+        const bool one = mn >= plo && mx <= phi && bin(mn) == bin(mx);
+        if (__ballot(!none && !one) == 0u) {
+          hist_add_lanes(hist, bin(mn), one ? static_cast<uint32_t>(kChunkPos) : 0u);
+          return true;
+        }
+      } else if (tally) {
+#pragma unroll
+        for (int u = 0; u < kChunkPos; ++u) {
+          gt += buf[u] > x ? 1u : 0u;
+          eq += buf[u] == x ? 1u : 0u;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kChunkPos; ++u) hist_add_wave(hist, bin(buf[u]), take(buf[u]));
+      return true;
     });
-  }
-  __device__ __forceinline__ void count(const Prefix& p, int d, int ib, uint32_t rmask,
-                                        uint32_t* hist) const {
-    count_digit_agg(*this, p, d, ib, rmask, hist);
+    if (tally) {
+      gt = wave_sum(gt);
+      eq = wave_sum(eq);
+      if (__lane_id() == 0) {
+        atomicAdd(&gt_eq[0], gt);
+        atomicAdd(&gt_eq[1], eq);
+      }
+    }
   }
 };
 
-// Exact selection of a whole row streamed from memory by one workgroup.
-// Radix rounds over the key digits (12, 10, 10 bits) run until the bucket
-// holding the k-th entry is taken whole or the threshold key T is known;
-// then, block by block, an ordered emission.  When only part of T's bucket
-// is taken, the emission takes every entry above T and the first `need`
-// entries equal to T in column order (the lowest columns among the ties),
-// counting the ties before each entry as it goes, so ties cost no rounds
-// over index digits.
+// Exact selection of a whole row streamed from memory by one workgroup,
+// given keys lo <= hi with lo <= T <= hi for the row's threshold key T (the
+// k-th largest; lo = 0, hi = 2^32 - 1 when nothing is known).  Radix rounds
+// over key digits (12, 10, 10 bits; those lo and hi share are skipped) run
+// until the bucket holding the k-th entry is taken whole or T is known.  With lo >= 1 the first round also counts the keys
+// above lo and equal to lo: fewer than k above and at least k at or above
+// make T = lo.  Then, block by block, an ordered emission, which stops once
+// k columns are out.  When only part of T's bucket is taken, the emission
+// takes every entry above T and the first `need` entries equal to T in
+// column order (the lowest columns among the ties), counting the ties
+// before each entry as it goes, so ties cost no rounds over index digits.
 template <int BLOCK>
 __device__ __forceinline__ void select_row_streamed(const float* row, int L, int k, const OutRow& out_row,
-                                                 uint32_t* hist, uint32_t* wtot, uint32_t* res) {
+                                                 uint32_t* hist, uint32_t* wtot, uint32_t* res,
+                                                 uint32_t lo, uint32_t hi) {
   constexpr int NW = BLOCK / kWave;
   const RowStream<BLOCK> src(row, L);
   const int ib = index_bits(L);
-  const uint32_t rmask = (1u << ib) - 1u;
   const uint32_t kk = static_cast<uint32_t>(k);
   const int tid = static_cast<int>(threadIdx.x);
   uint32_t need = kk;
-  Prefix pf{0, 0u, 0u};
+  // T's leading bits are those lo and hi share, and no key is above hi, so
+  // no entry lies in a bucket above that prefix: the rounds start at the
+  // last digit boundary within it (moving the digits instead would make
+  // them finer than the row's runs of nearby values, whose lanes the
+  // histogram adds at once).
+  if (lo > hi) {  // (not a bound pair: nothing is known)
+    lo = 0u;
+    hi = 0xFFFFFFFFu;
+  }
+  const int shared = lo == hi ? 32 : __clz(lo ^ hi);
+  const int start = shared == 32 ? 32
+                    : shared >= kFirstBits + kNextBits ? kFirstBits + kNextBits
+                    : shared >= kFirstBits ? kFirstBits : 0;
+  Prefix pf{start, start == 0 ? 0u : hi >> (32 - start), 0u};
   bool whole = false;  // the last bucket is taken whole
+  bool first = true;
   while (pf.bits < 32) {
     const int d = digit_bits(pf.bits, ib);
-    const int nb = 1 << d;
+    const bool wide = d > kNextBits;
+    const int nb = wide ? kFirstBins : kNextBins;  // the bins the search reads
     for (int i = tid; i < nb; i += BLOCK) hist[i] = 0;
+    if (tid == 0) {
+      res[7] = 0u;
+      res[8] = 0u;
+    }
     __syncthreads();
-    src.count(pf, d, ib, rmask, hist);
+    const bool tally = first && lo != 0u;
+    src.count(pf, d, hist, tally, lo, res + 7);
     __syncthreads();
+    if (tally) {
+      const uint32_t above = res[7], at = res[8];
+      if (above < kk && above + at >= kk) {
+        pf = Prefix{32, lo, 0u};
+        need = kk - above;
+        break;
+      }
+    }
+    first = false;
     const auto fixed = [need](uint32_t) { return need; };
-    if (d == kFirstBits) {
+    if (wide) {
       find_bucket_block<BLOCK, kFirstBins>(hist, fixed, res, wtot);
     } else {
       find_bucket_block<BLOCK, kNextBins>(hist, fixed, res, wtot);
@@ -1411,71 +1531,95 @@ __device__ __forceinline__ void select_row_streamed(const float* row, int L, int
       break;
     }
   }
+  // The emission's wavefront counts alternate between two LDS arrays (wtot
+  // and, free by now, the histogram's first words), so that one barrier
+  // per count suffices: a wavefront writes an array again only after a
+  // later barrier that every reader of its last contents has passed.
   uint32_t out_base = 0;
   if (whole) {
-    with_pred(pf, ib, rmask, [&](const auto& pred) {
-      src.blocks([&](const uint32_t (&buf)[kChunkPos], int e0) {
-        uint32_t n = 0;
+    // the selected entries are those with a key at or above the bucket's
+    // edge: exactly k of them
+    const uint32_t edge = prefix_edge(pf);
+    bool odd = false;
+    src.blocks([&](const uint32_t (&buf)[kChunkPos], int e0, bool) {
+      uint32_t* const wc = odd ? hist : wtot;
+      odd = !odd;
+      uint32_t mn, mx;
+      lane_range(buf, mn, mx);
+      uint32_t n = mn >= edge ? static_cast<uint32_t>(kChunkPos) : 0u;
+      if (!(mn >= edge || mx < edge)) {
 #pragma unroll
-        for (int u = 0; u < kChunkPos; ++u) n += pred.ge(buf[u], e0 + u * kWave) ? 1u : 0u;
-        uint32_t pos = out_base + wave_offset<BLOCK>(wave_sum(n), wtot);
-        uint32_t block_total = 0;
+        for (int u = 0; u < kChunkPos; ++u) n += buf[u] >= edge ? 1u : 0u;
+      }
+      const uint32_t wn = wave_sum(n);
+      uint32_t pos = out_base + wave_offset<BLOCK>(wn, wc);
+      uint32_t block_total = 0;
 #pragma unroll
-        for (int i = 0; i < NW; ++i) block_total += wtot[i];
+      for (int i = 0; i < NW; ++i) block_total += wc[i];
+      if (wn != 0u) {
 #pragma unroll
         for (int u = 0; u < kChunkPos; ++u) {
-          const int32_t j = e0 + u * kWave;
-          const bool sel = pred.ge(buf[u], j);
+          const bool sel = buf[u] >= edge;
           const uint64_t m = __ballot(sel);
           const uint32_t at = pos + lanes_below(m);
-          if (sel && at < kk) out_row.put(at, j);
+          if (sel && at < kk) out_row.put(at, e0 + u * kWave);
           pos += static_cast<uint32_t>(__popcll(m));
         }
-        out_base += block_total;
-        __syncthreads();  // wtot is reused
-      });
+      }
+      out_base += block_total;
+      return out_base < kk;
     });
+    __syncthreads();  // the output and the LDS are complete for the caller
     return;
   }
-  // T = pf.kp (the whole key); `need` entries equal to T are taken.  In a
-  // block, column order is (wavefront, position, lane).
+  // T = pf.kp (the whole key); `need` entries equal to T are taken.
   const uint32_t T = pf.kp;
   uint32_t tie_run = 0;  // entries equal to T in the earlier blocks
-  src.blocks([&](const uint32_t (&buf)[kChunkPos], int e0) {
+  src.blocks([&](const uint32_t (&buf)[kChunkPos], int e0, bool) {
+    uint32_t mn, mx;
+    lane_range(buf, mn, mx);
+    const bool any = __ballot(mx >= T) != 0u;  // (the wavefront has keys at or above T)
     uint32_t tw = 0;
+    if (any) {
 #pragma unroll
-    for (int u = 0; u < kChunkPos; ++u) tw += static_cast<uint32_t>(__popcll(__ballot(buf[u] == T)));
+      for (int u = 0; u < kChunkPos; ++u) tw += static_cast<uint32_t>(__popcll(__ballot(buf[u] == T)));
+    }
     uint32_t tr = tie_run + wave_offset<BLOCK>(tw, wtot);
     uint32_t tie_block = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) tie_block += wtot[i];
-    __syncthreads();  // wtot is reused
     uint32_t n = 0, selm = 0;
+    if (any) {
 #pragma unroll
-    for (int u = 0; u < kChunkPos; ++u) {
-      const bool tie = buf[u] == T;
-      const uint64_t m = __ballot(tie);
-      const bool sel = buf[u] > T || (tie && tr + lanes_below(m) < need);
-      selm |= sel ? (1u << u) : 0u;
-      n += sel ? 1u : 0u;
-      tr += static_cast<uint32_t>(__popcll(m));
+      for (int u = 0; u < kChunkPos; ++u) {
+        const bool tie = buf[u] == T;
+        const uint64_t m = __ballot(tie);
+        const bool sel = buf[u] > T || (tie && tr + lanes_below(m) < need);
+        selm |= sel ? (1u << u) : 0u;
+        n += sel ? 1u : 0u;
+        tr += static_cast<uint32_t>(__popcll(m));
+      }
+      n = wave_sum(n);
     }
-    uint32_t pos = out_base + wave_offset<BLOCK>(wave_sum(n), wtot);
+    uint32_t pos = out_base + wave_offset<BLOCK>(n, hist);
     uint32_t block_total = 0;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) block_total += wtot[i];
+    for (int i = 0; i < NW; ++i) block_total += hist[i];
+    if (n != 0u) {
 #pragma unroll
-    for (int u = 0; u < kChunkPos; ++u) {
-      const bool sel = ((selm >> u) & 1u) != 0u;
-      const uint64_t m = __ballot(sel);
-      const uint32_t at = pos + lanes_below(m);
-      if (sel && at < kk) out_row.put(at, e0 + u * kWave);
-      pos += static_cast<uint32_t>(__popcll(m));
+      for (int u = 0; u < kChunkPos; ++u) {
+        const bool sel = ((selm >> u) & 1u) != 0u;
+        const uint64_t m = __ballot(sel);
+        const uint32_t at = pos + lanes_below(m);
+        if (sel && at < kk) out_row.put(at, e0 + u * kWave);
+        pos += static_cast<uint32_t>(__popcll(m));
+      }
     }
     out_base += block_total;
     tie_run += tie_block;
-    __syncthreads();  // wtot is reused
+    return out_base < kk;
   });
+  __syncthreads();  // the output and the LDS are complete for the caller
 }
 
 // Adds N entries per lane of a wavefront to an LDS histogram: one atomic
@@ -2022,6 +2166,7 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
       });
     }
     done = edge >= max_lb;
+    if (tid == 0) res[9] = edge;  // (for the streamed selection: at most the row's threshold)
     // the slots read return to zero (other paths may use the workspace next;
     // the slotted union's were cleared as soon as they were read)
     if (!slotted) {
@@ -2035,7 +2180,14 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
     if (!done) __syncthreads();  // the streamed selection reuses the LDS
   }
   if (!done) {
-    select_row_streamed<BLOCK>(row_ptr, L, p.k, out_row, hist, wtot, res);
+    // Bounds on the row's threshold key T.  Below: the union is part of
+    // the row, so its k-th largest key (at least the edge of its bucket) is
+    // at most T; without the union, at least k candidates lie at or above
+    // the smallest chunk bound.  Above: every chunk's largest key is among
+    // its candidates (a bound is at most one of the chunk's own samples),
+    // except in a chunk of keys 1 alone, below every bound.
+    const uint32_t t_lo = exact_ok ? res[9] : (res[5] >= kk ? res[6] : 0u);
+    select_row_streamed<BLOCK>(row_ptr, L, p.k, out_row, hist, wtot, res, t_lo, max(res[11], 1u));
     if constexpr (VO) vo_rank_written<BLOCK>(row_ptr, L, p.k, out_row.p, comp);
   }
   if (!exact_ok) {

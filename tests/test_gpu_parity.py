@@ -348,6 +348,57 @@ def test_streamed_fallback_shortcuts(stride, k):
         assert_parity(w, got, label=f"{path} stride {stride} k {k}")
 
 
+def _structured_rows(rng, rows, stride):
+    """Rows built from runs: plateaus of random lengths and levels, ramps of
+    random slope (some within one float binade, so that many keys share
+    their leading bits), -inf or constant tails at random columns, and
+    mixtures, so that the streamed selection meets blocks whose lanes lie
+    in one histogram bin, outside the round's prefix, or straddle it."""
+    out = np.empty((rows, stride), dtype=np.float32)
+    j = np.arange(stride, dtype=np.float64)
+    for r in range(rows):
+        kind = r % 6
+        if kind == 0:    # plateaus
+            run = int(rng.integers(1, 400))
+            out[r] = np.floor(j / run).astype(np.float32) * np.float32(rng.choice([1.0, -1.0, 0.5]))
+        elif kind == 1:  # fine ramp: runs of equal values inside one binade
+            out[r] = (1.0 + j * 2.0 ** -int(rng.integers(24, 34))).astype(np.float32)
+        elif kind == 2:  # ramp with a random sign and offset
+            out[r] = (rng.uniform(-1e4, 1e4) + rng.choice([1.0, -1.0]) * j).astype(np.float32)
+        elif kind == 3:  # finite head, then a constant or -inf tail
+            f = int(rng.integers(0, stride))
+            out[r] = rng.choice([-np.inf, -7.0, 0.0])
+            out[r, :f] = rng.standard_normal(f).astype(np.float32)
+        elif kind == 4:  # few levels in long runs
+            lv = rng.standard_normal(int(rng.integers(2, 9))).astype(np.float32)
+            cuts = np.sort(rng.integers(0, stride, size=len(lv) - 1))
+            out[r] = lv[np.searchsorted(cuts, np.arange(stride), side="right")]
+        else:            # noise on one half, a plateau on the other
+            h = stride // 2
+            out[r, :h] = rng.standard_normal(h).astype(np.float32)
+            out[r, h:] = np.float32(rng.uniform(-3, 3))
+            if rng.random() < 0.5:
+                out[r] = out[r, ::-1]
+    return out
+
+
+@pytest.mark.parametrize("stride,k", [(131072, 1), (131072, 1024), (131072, 4096), (65536, 2048), (200000, 333)])
+def test_streamed_fallback_structured_rows(stride, k):
+    # rows of runs, ramps and tails, many of which the chunked path hands to
+    # its streamed selection; lengths random, some not a multiple of the
+    # streamed block
+    rng = np.random.default_rng(stride * 7 + k)
+    rows = 36
+    x = _structured_rows(rng, rows, stride)
+    flat = torch.from_numpy(x.reshape(-1).copy())
+    lengths = torch.from_numpy(rng.integers(k + 1, stride + 1, size=rows).astype(np.int32))
+    lengths[::4] = stride
+    w = workloads.Workload("structured", flat, stride, lengths, rows, k)
+    for path in ("auto", "chunks"):
+        got = run_gpu(w, path=path)
+        assert_parity(w, got, label=f"{path} stride {stride} k {k}")
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode", "long", "prefill", "adversarial"])
 def test_value_order_named_workloads(name):
     # the selected columns ranked by value (descending, ties by column), on
