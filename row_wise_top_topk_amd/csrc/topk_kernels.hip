@@ -1442,8 +1442,18 @@ struct RowStream {
           eq += buf[u] == x ? 1u : 0u;
         }
       }
+      // entry by entry: aggregated per position where the first position's
+      // 64 entries share a bin (runs of equal or nearby values), else each
+      // alone (scattered values, whose adds rarely meet in one bin)
+      const uint32_t b00 = bin(buf[0]);
+      if (__ballot(b00 != static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b00)))) == 0u) {
 #pragma unroll
-      for (int u = 0; u < kChunkPos; ++u) hist_add_wave(hist, bin(buf[u]), take(buf[u]));
+        for (int u = 0; u < kChunkPos; ++u) hist_add_wave(hist, bin(buf[u]), take(buf[u]));
+      } else {
+#pragma unroll
+        for (int u = 0; u < kChunkPos; ++u)
+          if (take(buf[u])) atomicAdd(&hist[bin(buf[u])], 1u);
+      }
       return true;
     });
     if (tally) {
@@ -1578,9 +1588,10 @@ __device__ __forceinline__ void select_row_streamed(const float* row, int L, int
   src.blocks([&](const uint32_t (&buf)[kChunkPos], int e0, bool) {
     uint32_t mn, mx;
     lane_range(buf, mn, mx);
-    const bool any = __ballot(mx >= T) != 0u;  // (the wavefront has keys at or above T)
+    const bool any = __ballot(mx >= T) != 0u;                 // keys at or above T
+    const bool ties = __ballot(mn <= T && T <= mx) != 0u;     // keys that may equal T
     uint32_t tw = 0;
-    if (any) {
+    if (ties) {
 #pragma unroll
       for (int u = 0; u < kChunkPos; ++u) tw += static_cast<uint32_t>(__popcll(__ballot(buf[u] == T)));
     }
@@ -1589,7 +1600,7 @@ __device__ __forceinline__ void select_row_streamed(const float* row, int L, int
 #pragma unroll
     for (int i = 0; i < NW; ++i) tie_block += wtot[i];
     uint32_t n = 0, selm = 0;
-    if (any) {
+    if (ties) {
 #pragma unroll
       for (int u = 0; u < kChunkPos; ++u) {
         const bool tie = buf[u] == T;
@@ -1598,6 +1609,14 @@ __device__ __forceinline__ void select_row_streamed(const float* row, int L, int
         selm |= sel ? (1u << u) : 0u;
         n += sel ? 1u : 0u;
         tr += static_cast<uint32_t>(__popcll(m));
+      }
+      n = wave_sum(n);
+    } else if (any) {
+#pragma unroll
+      for (int u = 0; u < kChunkPos; ++u) {
+        const bool sel = buf[u] > T;
+        selm |= sel ? (1u << u) : 0u;
+        n += sel ? 1u : 0u;
       }
       n = wave_sum(n);
     }
@@ -1654,7 +1673,7 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
   __shared__ uint16_t scol[kChunkCap];
   __shared__ uint32_t wq[4 * NW];
   __shared__ uint32_t wtot[NW];
-  __shared__ uint32_t res[12];
+  __shared__ uint32_t res[13];
   const int tid = threadIdx.x;
   const int G = p.G;
   const int64_t row = item / G;
@@ -1992,11 +2011,17 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
     // offsets of the chunks' candidates in the packed union, total, bounds,
     // largest key
     uint32_t run = 0, lo = 0xFFFFFFFFu, hi = 0u, bad = 0u, mc = 0u, km = 0u;
+    uint32_t cnt0 = 0u, km0 = 0u;  // this lane's chunk of the first 64
     for (int b0 = 0; b0 < Gr; b0 += kWave) {
       const int c = b0 + tid;
       const uint32_t cnt = c < Gr ? g_load(&counts[c]) : 0u;
       const uint32_t bnd = c < Gr ? g_load(&bounds[c]) : 0u;
-      km = max(km, c < Gr ? g_load(&kmaxs[c]) : 0u);
+      const uint32_t kmc = c < Gr ? g_load(&kmaxs[c]) : 0u;
+      km = max(km, kmc);
+      if (b0 == 0) {
+        cnt0 = cnt;
+        km0 = kmc;
+      }
       const uint32_t incl = wave_inclusive_sum(cnt);
       if (c < Gr) coff[c] = run + incl - cnt;
       run += static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
@@ -2012,6 +2037,11 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
     bad = wave_max(bad);
     mc = wave_max(mc);
     km = wave_max(km);
+    // Union entries at or above the largest bound come only from chunks
+    // whose largest key reaches it: with fewer than k of those the union's
+    // k-th largest lies below that bound and the union cannot be exact
+    // (counted when each lane holds one chunk).
+    const uint32_t reach = wave_sum(km0 >= hi ? cnt0 : 0u);
     if (tid == 0) {
       coff[Gr] = run;
       res[5] = run;
@@ -2020,6 +2050,7 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
       res[8] = bad;
       res[10] = mc;
       res[11] = km;
+      res[12] = Gr <= kWave && reach < kk ? 1u : 0u;
     }
   }
   __syncthreads();
@@ -2033,7 +2064,7 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
   const bool fits = res[8] == 0u && utotal >= kk;
   const bool slotted = fits && res[10] <= 4u * Wg;
   const bool exact_ok =
-      fits && (slotted || utotal <= static_cast<uint32_t>(BLOCK * kUnionPerThread));
+      fits && (slotted || utotal <= static_cast<uint32_t>(BLOCK * kUnionPerThread)) && res[12] == 0u;
   bool done = false;
   if (exact_ok) {
     if (slotted) {
