@@ -19,7 +19,8 @@ from gpu_util import SENTINEL, assert_parity, device_view, expected
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-KINDS = ["normal", "bf16", "levels", "equal", "outliers", "ramp"]
+KINDS = ["normal", "bf16", "levels", "equal", "outliers", "ramp", "tail", "plateau", "fineramp",
+         "descending"]
 MAX_ELEMS = 1_500_000       # per case, so that the oracle stays fast
 
 

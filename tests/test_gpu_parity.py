@@ -127,9 +127,10 @@ def test_random_stress_chunked_path():
     # random lengths and k, smooth and tied kinds; one workspace for every
     # call, left all zero each time
     rng = np.random.default_rng(4321)
-    kinds = ["normal", "bf16", "levels", "equal", "outliers", "ramp"]
+    kinds = ["normal", "bf16", "levels", "equal", "outliers", "ramp", "tail", "plateau", "fineramp",
+             "descending"]
     ws = None
-    for trial in range(36):
+    for trial in range(60):
         rows = int(rng.integers(1, 9))
         stride = int(rng.integers(16385, 400001))
         k = int(rng.integers(1, 4097))

@@ -185,7 +185,11 @@ def make_custom(num_rows: int, row_stride: int, lengths, k: int, seed: int,
 
     ``kind``: ``normal`` (N(0,1)), ``bf16`` (N(0,1) rounded to bf16, many ties),
     ``levels`` (``levels`` distinct values), ``equal`` (one value), ``ramp``
-    (ascending ``x_j = j``), ``outliers`` (N(0,1) with 0.5 % N(4,1)).
+    (ascending ``x_j = j``), ``outliers`` (N(0,1) with 0.5 % N(4,1)),
+    ``tail`` (an N(0,1) head of random length per row, then ``-inf``),
+    ``plateau`` (``floor(j / run)`` with a random run per row), ``fineramp``
+    (``1 + j * 2**-30``: runs of 128 equal values inside one binade),
+    ``descending`` (``x_j = -j``).
     """
     g = torch.Generator().manual_seed(seed)
     lengths = torch.as_tensor(lengths, dtype=torch.int32).reshape(-1)
@@ -204,6 +208,19 @@ def make_custom(num_rows: int, row_stride: int, lengths, k: int, seed: int,
     elif kind == "outliers":
         mask = torch.rand(num_rows, row_stride, generator=g) < 0.005
         rows[mask] = 4.0 + torch.randn(int(mask.sum()), generator=g, dtype=torch.float32)
+    elif kind == "tail":
+        heads = torch.randint(0, row_stride + 1, (num_rows,), generator=g)
+        col = torch.arange(row_stride).unsqueeze(0)
+        rows.masked_fill_(col >= heads.unsqueeze(1), float("-inf"))
+    elif kind == "plateau":
+        runs = torch.randint(1, 300, (num_rows, 1), generator=g).to(torch.float64)
+        j = torch.arange(row_stride, dtype=torch.float64).unsqueeze(0)
+        rows = torch.floor(j / runs).to(torch.float32)
+    elif kind == "fineramp":
+        j = torch.arange(row_stride, dtype=torch.float64)
+        rows = (1.0 + j * 2.0 ** -30).to(torch.float32).repeat(num_rows, 1)
+    elif kind == "descending":
+        rows = (-torch.arange(row_stride, dtype=torch.float32)).repeat(num_rows, 1)
     elif kind != "normal":
         raise ValueError(f"unknown kind {kind!r}")
     flat = rows.reshape(-1).contiguous()
