@@ -1400,9 +1400,9 @@ struct RowStream {
   // Histogram of key digit d below the key prefix p (p.bits < 32; 0: every
   // entry of the row).  A wavefront whose lanes each have their 16 keys
   // outside the prefix or in one bin adds per lane (one atomic when the
-  // lanes share the bin); other blocks add entry by entry, aggregated per
-  // position (hist_add_wave).  With `tally`, also the row's keys above x
-  // and equal to x, added to gt_eq[0] and gt_eq[1] (x >= 1).
+  // lanes share the bin); other blocks add entry by entry (see below).
+  // With `tally`, also the row's keys above x and equal to x, added to
+  // gt_eq[0] and gt_eq[1] (x >= 1).
   __device__ __forceinline__ void count(const Prefix& p, int d, uint32_t* hist, bool tally,
                                         uint32_t x, uint32_t* gt_eq) const {
     const int sh = 32 - p.bits;  // bits below the prefix
