@@ -454,12 +454,16 @@ __device__ __forceinline__ Prefix finish_small(const Src& src, uint32_t kp, int 
 // digits and spreads the entries over many bins.  A bucket of at most 64
 // entries is then finished by finish_small, a larger one by rounds_local.
 // hist_zero: the caller has already zeroed hist[0..kFirstBins) before a
-// workgroup barrier.  res[3] is overwritten.  Returns the final prefix.
+// workgroup barrier.  equal_ok: the caller's emission keeps only the first
+// `need` selected entries in column order, so when lo == hi (every key the
+// same, nothing above it) the whole key is returned after the one round,
+// without rounds over the columns.  res[3] is overwritten.  Returns the
+// final prefix.
 template <int BLOCK, class Src>
 __device__ __forceinline__ Prefix rounds_window(const Src& src, uint32_t lo, uint32_t hi,
                                                 uint32_t need, int ib, uint32_t* hist,
                                                 uint32_t* res, uint32_t* wt,
-                                                bool hist_zero = false) {
+                                                bool hist_zero = false, bool equal_ok = false) {
   int s = 0;
   while ((hi >> s) - (lo >> s) >= static_cast<uint32_t>(kFirstBins)) ++s;
   const uint32_t base = lo >> s;
@@ -477,7 +481,7 @@ __device__ __forceinline__ Prefix rounds_window(const Src& src, uint32_t lo, uin
   const uint32_t b = res[0], gt = res[1], cnt = res[2];
   need -= gt;
   const Prefix p{32 - s, base + b, 0u};
-  if (cnt == need) return p;
+  if (cnt == need || (equal_ok && lo == hi)) return p;
   if (cnt <= static_cast<uint32_t>(kWave)) return finish_small<BLOCK>(src, base + b, s, need, ib, hist, res);
   return rounds_local<BLOCK>(src, p, need, ib, hist, res, wt);
 }

@@ -2128,7 +2128,13 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
     const uint32_t kmax = res[11];
     // slotted: the histogram was cleared before the counts' barrier; packed:
     // its words held the chunk map, rounds_window clears them
-    const Prefix pf = rounds_window<BLOCK>(un, min_lb, kmax, kk, ib, hist, res, wtot, slotted);
+    // Every candidate key lies in [min_lb, kmax].  When the two meet, every
+    // candidate equals the row's largest key T, nothing lies above T, and the
+    // first k candidates in the union's (column) order are the selection:
+    // "key >= T" with the emission's cap at k, no rounds over the columns
+    // (a chunk publishes its first k ties at most, in column order).  The
+    // value-order emission ranks exactly k entries, so it takes the rounds.
+    const Prefix pf = rounds_window<BLOCK>(un, min_lb, kmax, kk, ib, hist, res, wtot, slotted, !VO);
     // every selected key is at least the selected bucket's lower edge
     const uint32_t edge = prefix_edge(pf);
     if (edge >= max_lb) {
