@@ -329,6 +329,24 @@ struct OutRow {
   __device__ __forceinline__ void put(uint32_t at, int32_t j) const { p[at] = map(j); }
 };
 
+// Writes columns staged in LDS, cols[0..n), to out_row[0..n) in order: 16
+// bytes a lane when the row is 16-byte aligned and n a multiple of 4, else
+// 4.  Every thread of the workgroup takes part; the caller synchronises
+// before (the staging is complete).
+template <int BLOCK>
+__device__ __forceinline__ void write_staged(const OutRow& out_row, const int32_t* cols, uint32_t n) {
+  const uint32_t tid = threadIdx.x;
+  if ((reinterpret_cast<uintptr_t>(out_row.p) & 15u) == 0 && (n & 3u) == 0) {
+    for (uint32_t i = 4u * tid; i < n; i += 4u * BLOCK) {
+      const int4 v = *reinterpret_cast<const int4*>(cols + i);
+      *reinterpret_cast<int4*>(out_row.p + i) =
+          int4{out_row.map(v.x), out_row.map(v.y), out_row.map(v.z), out_row.map(v.w)};
+    }
+  } else {
+    for (uint32_t i = tid; i < n; i += BLOCK) out_row.put(i, cols[i]);
+  }
+}
+
 // Writes the chunk's selected elements (pred.ge) to out_row[base ...] in
 // ascending column order: a first pass counts each wavefront's selections,
 // then each position's selected lanes are placed with a ballot.
@@ -970,6 +988,12 @@ __device__ __forceinline__ void stream_item(const Params& p, int64_t row) {
   constexpr int kVoStage = kFirstBins / 2;
   uint64_t* const stage = comp + kVoStage;
   const bool vo_lds = VO && p.k <= kVoStage;
+  // Otherwise the selected columns are staged in LDS at their ranks and
+  // written out in order: a lane's selected entries are a run of ranks, so
+  // storing them directly would spread each store instruction's 64 lanes
+  // over the whole output row.  (The list holds at most 6144 entries, so k
+  // fits the union's 12288 words.)
+  int32_t* const cols = reinterpret_cast<int32_t*>(lds.u.list);
   with_pred(pf, ib, rmask, [&](const auto& pred) {
     uint32_t n = 0;
 #pragma unroll
@@ -985,13 +1009,17 @@ __device__ __forceinline__ void stream_item(const Params& p, int64_t row) {
           if (vo_lds) {
             stage[pos] = vo_composite(lst.key[u], lst.col[u]);
           } else {
-            out_row.put(pos, lst.col[u]);
+            cols[pos] = lst.col[u];
           }
         }
         ++pos;
       }
     }
   });
+  if (!vo_lds) {
+    __syncthreads();  // the staged columns are complete
+    write_staged<BLOCK>(out_row, cols, kk);
+  }
   if constexpr (VO) {
     if (vo_lds) {
       __syncthreads();  // the staged composites are complete
@@ -2189,17 +2217,7 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
           }
         }
         __syncthreads();
-        if ((reinterpret_cast<uintptr_t>(out_row.p) & 15u) == 0 && (kk & 3u) == 0) {
-          for (uint32_t i = 4u * static_cast<uint32_t>(tid); i < kk; i += 4u * BLOCK) {
-            const uint4 v = *reinterpret_cast<const uint4*>(stage + i);
-            *reinterpret_cast<int4*>(out_row.p + i) =
-                int4{out_row.map(static_cast<int32_t>(v.x)), out_row.map(static_cast<int32_t>(v.y)),
-                     out_row.map(static_cast<int32_t>(v.z)), out_row.map(static_cast<int32_t>(v.w))};
-          }
-        } else {
-          for (uint32_t i = static_cast<uint32_t>(tid); i < kk; i += BLOCK)
-            out_row.put(i, static_cast<int32_t>(stage[i]));
-        }
+        write_staged<BLOCK>(out_row, reinterpret_cast<const int32_t*>(stage), kk);
       });
     }
     done = edge >= max_lb;

@@ -428,6 +428,28 @@ def test_value_order_k_and_ties(k, kind):
     assert np.array_equal(out.cpu().numpy(), exp)
 
 
+@pytest.mark.parametrize("order", ["column", "value"])
+@pytest.mark.parametrize("k", [2049, 2500, 3000, 4096])
+def test_streaming_list_large_k(k, order):
+    # the streaming kernel's filtered list with k above the value-order
+    # staging limit (2048): the columns are staged in LDS and written in
+    # order, with and without 16-byte rows (k odd or a multiple of 4), and in
+    # value order ranked from the written row
+    stride = 32768
+    lengths = [32768, 32767, 30001, 20000, 16385, 12289, 9000, k, 5]
+    assert mt.plan_describe_for(len(lengths), stride, k, path="local")["elems_per_thread"] == 64
+    for kind in ("normal", "bf16"):
+        w = workloads.make_custom(len(lengths), stride, lengths, k, seed=k + len(kind), kind=kind)
+        logits, lens = device_view(w)
+        out = torch.full((w.num_rows, k), SENTINEL, dtype=torch.int32, device="cuda:0")
+        mt.topk_indices(logits, lens, k, out=out, path="local", order=order)
+        torch.cuda.synchronize()
+        exp = oracle_topk(w.flat.numpy(), stride, w.lengths.numpy(), w.num_rows, k, order=order)
+        got = out.cpu().numpy()
+        bad = np.nonzero(np.any(got != exp, axis=1))[0]
+        assert bad.size == 0, f"k={k} {order} {kind}: rows {bad.tolist()} differ"
+
+
 def test_value_order_rejects_bad_arguments():
     w = workloads.make_custom(2, 8192, [8192, 100], 4097, seed=5)
     logits, lens = device_view(w)
