@@ -101,6 +101,11 @@ __device__ __forceinline__ void g_store64(uint64_t* p, uint64_t v) {
 // Cache-policy operand of the buffer intrinsics that gives sc1, the policy of
 // the device-scope relaxed atomic loads and stores above on gfx950.
 constexpr int kCoherent = 16;
+// Cache-policy operand for rows streamed once: nt, the streaming hint.  A
+// 537 MB read of one row per workgroup measured 6.86 TB/s with it against
+// 6.12 TB/s with the default policy.  (Paths that read a row again soon
+// after, from the caches, keep the default.)
+constexpr int kReadOnce = 2;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -711,7 +716,7 @@ struct StreamGeom {
     const int e = elem(c);
 #pragma unroll
     for (int u = 0; u < kChunkPos; ++u)
-      buf[u] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (e + u * kWave) * 4, 0, 0);
+      buf[u] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (e + u * kWave) * 4, 0, kReadOnce);
   }
 
   // True if every position of chunk c lies inside [llo, lhi) (uniform).
@@ -896,7 +901,7 @@ __device__ __forceinline__ void stream_item(const Params& p, int64_t row) {
     const int e = g.elem(0);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      smp[q] = __builtin_amdgcn_raw_buffer_load_b32(g.rsrc, (e + q * QS * kWave) * 4, 0, 0);
+      smp[q] = __builtin_amdgcn_raw_buffer_load_b32(g.rsrc, (e + q * QS * kWave) * 4, 0, kReadOnce);
   }
   uint32_t bufs[kStreamBufs][kChunkPos];
 #pragma unroll
