@@ -400,6 +400,20 @@ __device__ __forceinline__ OutRow out_row_of(const Params& p, int64_t row) {
   return o;
 }
 
+// ceil(a * b / c) for the sample shares of k below (c >= 1).  The product
+// fits 32 bits whenever k is below about 170000, and a 32-bit division on
+// the scalar unit takes a tenth of the instructions of a 64-bit one, which
+// every wavefront would otherwise run on the way to its bound.
+__device__ __forceinline__ uint32_t ceil_mul_div(uint32_t a, uint32_t b, uint32_t c) {
+  const uint64_t num = static_cast<uint64_t>(a) * b;
+  if ((num >> 32) == 0u) {
+    const uint32_t n = static_cast<uint32_t>(num);
+    const uint32_t q = n / c;
+    return q + (q * c != n ? 1u : 0u);
+  }
+  return static_cast<uint32_t>((num + c - 1) / c);
+}
+
 __device__ __forceinline__ int index_bits(int L) {
   // bits needed for column indices 0..L-1 (L >= 2 here)
   return 32 - __clz(static_cast<uint32_t>(L - 1));
@@ -441,16 +455,17 @@ struct __attribute__((aligned(16))) RowLds {
   uint32_t res[4];
 };
 
-// The filtered list, kListPerThread entries per thread in registers: thread
-// t holds list entries [t*per, t*per + per) (column order); unused entries
-// have key 0.
+// The filtered list, N entries per thread in registers: thread t holds list
+// entries [t*per, t*per + per) (column order, per <= N); unused entries have
+// key 0.
+template <int N = kListPerThread>
 struct RegList {
-  uint32_t key[kListPerThread];
-  int32_t col[kListPerThread];
+  uint32_t key[N];
+  int32_t col[N];
   template <class F>
   __device__ __forceinline__ void operator()(F f) const {
 #pragma unroll
-    for (int u = 0; u < kListPerThread; ++u) f(key[u], col[u]);
+    for (int u = 0; u < N; ++u) f(key[u], col[u]);
   }
   __device__ __forceinline__ void count(const Prefix& p, int d, int ib, uint32_t rmask,
                                         uint32_t* hist) const {
@@ -480,8 +495,7 @@ __device__ __forceinline__ uint32_t sample_bound(const uint32_t (&raw)[E], int L
     find_bucket_wave_nb<kFirstBins>(
         lds.hist,
         [&](uint32_t ns) {
-          return static_cast<uint32_t>((5ull * static_cast<uint64_t>(k) * ns + 4ull * L - 1) /
-                                       (4ull * L)) + 8u;
+          return ceil_mul_div(5u * static_cast<uint32_t>(k), ns, 4u * static_cast<uint32_t>(L)) + 8u;
         },
         lds.res);
   }
@@ -551,7 +565,7 @@ __device__ __forceinline__ void select_row(uint32_t (&raw)[E], const Chunk& ch, 
       // region w(i), offset i - pre[w(i)]
       const uint32_t per = (total + BLOCK - 1) / BLOCK;
       const uint32_t first = threadIdx.x * per;
-      RegList lst;
+      RegList<> lst;
 #pragma unroll
       for (int u = 0; u < kListPerThread; ++u) {
         const uint32_t i = first + u;
@@ -852,6 +866,112 @@ __device__ __forceinline__ uint32_t filter_stream(const StreamGeom<BLOCK, NP>& g
   return cnt;
 }
 
+// The streaming kernel's selection from its filtered list (each wavefront's
+// cw entries in its LDS region, keys in [lb, ...]): the list in registers, N
+// entries a thread, a windowed radix round, and the ordered emission.
+template <int BLOCK, int N, bool VO>
+__device__ __forceinline__ void stream_list_select(const Params& p, StreamLds<BLOCK>& lds, uint32_t cw,
+                                                   uint32_t lb, int L, const OutRow& out_row,
+                                                   const float* row_ptr, uint64_t* comp) {
+  static_assert(N % 4 == 0 && N <= kListPerThread, "16-byte LDS reads");
+  const int tid = threadIdx.x;
+  const uint32_t w = wave_id();
+  const uint32_t kk = static_cast<uint32_t>(p.k);
+  const int ib = index_bits(L);
+  const uint32_t rmask = (1u << ib) - 1u;
+  // lane l takes entries [l*per, l*per+per) of its wavefront's region, per a
+  // multiple of 4 (16-byte LDS reads)
+  RegList<N> lst;
+  {
+    constexpr int kCols = StreamLds<BLOCK>::kListCols;
+    const uint32_t per = (((cw + kWave - 1) / kWave) + 3u) & ~3u;
+    const uint32_t first = __lane_id() * per;
+    const uint32_t* region = lds.u.list + w * kStreamRegion;
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      const uint32_t i0 = first + 4u * q;
+      uint4 r = make_uint4(0u, 0u, 0u, 0u), c = make_uint4(0u, 0u, 0u, 0u);
+      if (4u * q < per) {
+        r = *reinterpret_cast<const uint4*>(region + i0);
+        c = *reinterpret_cast<const uint4*>(region + kCols + i0);
+      }
+      const uint32_t rv[4] = {r.x, r.y, r.z, r.w};
+      const uint32_t cv[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bool ok = 4u * q + t < per && i0 + t < cw;
+        lst.key[4 * q + t] = ok ? order_key_bits(rv[t]) : 0u;
+        lst.col[4 * q + t] = static_cast<int32_t>(cv[t]);
+      }
+    }
+    uint32_t mx = 0;
+#pragma unroll
+    for (int u = 0; u < N; ++u) mx = max(mx, lst.key[u]);
+    mx = wave_max(mx);
+    if (__lane_id() == 0) atomicMax(&lds.res[3], mx);
+  }
+  __syncthreads();  // the list's LDS becomes the histogram
+  // every listed key lies in [lb, largest]
+  const uint32_t kmax = lds.res[3];
+  const Prefix pf = rounds_window<BLOCK>(lst, lb, kmax, kk, ib, lds.u.hist, lds.res, lds.wtot);
+  // VO: with k <= 2048 the selected composites are staged in LDS at their
+  // column-order ranks (the list's registers end here) and ranked by value
+  // from there: union words [0, 16 KB) bins, [16, 32) staging, [32, 48) the
+  // scattered composites.  A larger k ranks the written row instead.
+  constexpr int kVoStage = kFirstBins / 2;
+  uint64_t* const stage = comp + kVoStage;
+  const bool vo_lds = VO && p.k <= kVoStage;
+  // Otherwise the selected columns are staged in LDS at their ranks and
+  // written out in order: a lane's selected entries are a run of ranks, so
+  // storing them directly would spread each store instruction's 64 lanes
+  // over the whole output row.  (The list holds at most 6144 entries, so k
+  // fits the union's 12288 words.)
+  int32_t* const cols = reinterpret_cast<int32_t*>(lds.u.list);
+  with_pred(pf, ib, rmask, [&](const auto& pred) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int u = 0; u < N; ++u) n += pred.ge(lst.key[u], lst.col[u]) ? 1u : 0u;
+    const uint32_t incl = wave_inclusive_sum(n);
+    const uint32_t wtotal =
+        static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+    uint32_t pos = wave_offset<BLOCK>(wtotal, lds.wtot) + incl - n;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      if (pred.ge(lst.key[u], lst.col[u])) {
+        if (pos < kk) {
+          if (vo_lds) {
+            stage[pos] = vo_composite(lst.key[u], lst.col[u]);
+          } else {
+            cols[pos] = lst.col[u];
+          }
+        }
+        ++pos;
+      }
+    }
+  });
+  if (!vo_lds) {
+    __syncthreads();  // the staged columns are complete
+    write_staged<BLOCK>(out_row, cols, kk);
+  }
+  if constexpr (VO) {
+    if (vo_lds) {
+      __syncthreads();  // the staged composites are complete
+      const int m = p.k;
+      vo_bucket_rank<BLOCK>(
+          [&](auto f) {
+#pragma unroll 1
+            for (int i = tid; i < m; i += BLOCK) {
+              const uint64_t c = stage[i];
+              f(static_cast<uint32_t>(c >> 32), vo_column(c));
+            }
+          },
+          prefix_edge(pf), kmax, m, out_row.p, lds.u.hist, comp + 2 * kVoStage, lds.wtot, lds.res);
+    } else {
+      vo_rank_written<BLOCK>(row_ptr, L, p.k, out_row.p, comp);
+    }
+  }
+}
+
 template <int BLOCK, int NP, bool VO>
 __device__ __forceinline__ void stream_item(const Params& p, int64_t row) {
   constexpr int NW = BLOCK / kWave;
@@ -924,7 +1044,7 @@ __device__ __forceinline__ void stream_item(const Params& p, int64_t row) {
   find_bucket_block<BLOCK, kFirstBins>(
       lds.u.hist,
       [&](uint32_t ns) {
-        return static_cast<uint32_t>((5ull * kk * ns + 4ull * L - 1) / (4ull * L)) + 8u;
+        return ceil_mul_div(5u * kk, ns, 4u * static_cast<uint32_t>(L)) + 8u;
       },
       lds.res, lds.wtot);
   __syncthreads();
@@ -937,11 +1057,12 @@ __device__ __forceinline__ void stream_item(const Params& p, int64_t row) {
   if (__lane_id() == 0) lds.wtot[w] = cw;
   if (tid == 0) lds.res[3] = 0u;  // the list's largest key, below
   __syncthreads();
-  uint32_t total = 0, over = 0;
+  uint32_t total = 0, over = 0, maxcw = 0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     const uint32_t c = lds.wtot[i];
     total += c;
+    maxcw = max(maxcw, c);
     over |= c > static_cast<uint32_t>(kStreamRegion) ? 1u : 0u;
   }
   if (over || total < kk) {
@@ -951,96 +1072,12 @@ __device__ __forceinline__ void stream_item(const Params& p, int64_t row) {
     return;
   }
 
-  // the wavefront's list in registers: lane l takes entries [l*per, l*per+per)
-  // of its region, per a multiple of 4 (16-byte LDS reads)
-  RegList lst;
-  {
-    constexpr int kCols = StreamLds<BLOCK>::kListCols;
-    const uint32_t per = (((cw + kWave - 1) / kWave) + 3u) & ~3u;
-    const uint32_t first = __lane_id() * per;
-    const uint32_t* region = lds.u.list + w * kStreamRegion;
-#pragma unroll
-    for (int q = 0; q < kListPerThread / 4; ++q) {
-      const uint32_t i0 = first + 4u * q;
-      uint4 r = make_uint4(0u, 0u, 0u, 0u), c = make_uint4(0u, 0u, 0u, 0u);
-      if (4u * q < per) {
-        r = *reinterpret_cast<const uint4*>(region + i0);
-        c = *reinterpret_cast<const uint4*>(region + kCols + i0);
-      }
-      const uint32_t rv[4] = {r.x, r.y, r.z, r.w};
-      const uint32_t cv[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bool ok = 4u * q + t < per && i0 + t < cw;
-        lst.key[4 * q + t] = ok ? order_key_bits(rv[t]) : 0u;
-        lst.col[4 * q + t] = static_cast<int32_t>(cv[t]);
-      }
-    }
-    uint32_t mx = 0;
-#pragma unroll
-    for (int u = 0; u < kListPerThread; ++u) mx = max(mx, lst.key[u]);
-    mx = wave_max(mx);
-    if (__lane_id() == 0) atomicMax(&lds.res[3], mx);
-  }
-  __syncthreads();  // the list's LDS becomes the histogram
-  // every listed key lies in [lb, largest]
-  const uint32_t kmax = lds.res[3];
-  const Prefix pf = rounds_window<BLOCK>(lst, lb, kmax, kk, ib, lds.u.hist, lds.res, lds.wtot);
-  // VO: with k <= 2048 the selected composites are staged in LDS at their
-  // column-order ranks (the list's registers end here) and ranked by value
-  // from there: union words [0, 16 KB) bins, [16, 32) staging, [32, 48) the
-  // scattered composites.  A larger k ranks the written row instead.
-  constexpr int kVoStage = kFirstBins / 2;
-  uint64_t* const stage = comp + kVoStage;
-  const bool vo_lds = VO && p.k <= kVoStage;
-  // Otherwise the selected columns are staged in LDS at their ranks and
-  // written out in order: a lane's selected entries are a run of ranks, so
-  // storing them directly would spread each store instruction's 64 lanes
-  // over the whole output row.  (The list holds at most 6144 entries, so k
-  // fits the union's 12288 words.)
-  int32_t* const cols = reinterpret_cast<int32_t*>(lds.u.list);
-  with_pred(pf, ib, rmask, [&](const auto& pred) {
-    uint32_t n = 0;
-#pragma unroll
-    for (int u = 0; u < kListPerThread; ++u) n += pred.ge(lst.key[u], lst.col[u]) ? 1u : 0u;
-    const uint32_t incl = wave_inclusive_sum(n);
-    const uint32_t wtotal =
-        static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
-    uint32_t pos = wave_offset<BLOCK>(wtotal, lds.wtot) + incl - n;
-#pragma unroll
-    for (int u = 0; u < kListPerThread; ++u) {
-      if (pred.ge(lst.key[u], lst.col[u])) {
-        if (pos < kk) {
-          if (vo_lds) {
-            stage[pos] = vo_composite(lst.key[u], lst.col[u]);
-          } else {
-            cols[pos] = lst.col[u];
-          }
-        }
-        ++pos;
-      }
-    }
-  });
-  if (!vo_lds) {
-    __syncthreads();  // the staged columns are complete
-    write_staged<BLOCK>(out_row, cols, kk);
-  }
-  if constexpr (VO) {
-    if (vo_lds) {
-      __syncthreads();  // the staged composites are complete
-      const int m = p.k;
-      vo_bucket_rank<BLOCK>(
-          [&](auto f) {
-#pragma unroll 1
-            for (int i = tid; i < m; i += BLOCK) {
-              const uint64_t c = stage[i];
-              f(static_cast<uint32_t>(c >> 32), vo_column(c));
-            }
-          },
-          prefix_edge(pf), kmax, m, out_row.p, lds.u.hist, comp + 2 * kVoStage, lds.wtot, lds.res);
-    } else {
-      vo_rank_written<BLOCK>(row_ptr, L, p.k, out_row.p, comp);
-    }
+  // the lists in registers: N entries a thread, the fewest that hold the
+  // longest wavefront list (a lane takes a multiple of 4 entries)
+  if (maxcw <= 8u * kWave) {
+    stream_list_select<BLOCK, 8, VO>(p, lds, cw, lb, L, out_row, row_ptr, comp);
+  } else {
+    stream_list_select<BLOCK, kListPerThread, VO>(p, lds, cw, lb, L, out_row, row_ptr, comp);
   }
 }
 
@@ -1785,7 +1822,7 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
   int ns = 0;
 #pragma unroll
   for (int v = 0; v < NW; ++v) ns += min(max(clen - v * kWave * E, 0), kWave * kChunkSamples);
-  const uint32_t nd = static_cast<uint32_t>((3ull * kk * ns + 2ull * L - 1) / (2ull * L)) + 16u;
+  const uint32_t nd = ceil_mul_div(3u * kk, static_cast<uint32_t>(ns), 2u * static_cast<uint32_t>(L)) + 16u;
   // When nd is small against the 512 threads, each thread contributes only
   // the largest of its samples: the nd largest samples then lie in nearly
   // nd different threads, so the nd-th largest maximum is a bound just below
