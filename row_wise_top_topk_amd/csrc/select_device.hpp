@@ -552,7 +552,8 @@ __device__ __forceinline__ void vo_sort_store(uint64_t* comp, int m, int32_t* ou
   for (int i = m + static_cast<int>(threadIdx.x); i < n; i += BLOCK) comp[i] = 0ull;  // sorts last
   __syncthreads();
   bitonic_sort_desc<BLOCK>(comp, n);
-  for (int i = static_cast<int>(threadIdx.x); i < m; i += BLOCK) out[i] = vo_column(comp[i]);
+  // (nontemporal stores: the index rows are not read again here)
+  for (int i = static_cast<int>(threadIdx.x); i < m; i += BLOCK) __builtin_nontemporal_store(vo_column(comp[i]), out + i);
 }
 
 // Ranks by value the m columns this workgroup has just written to out[0..m)
@@ -691,7 +692,7 @@ __device__ __forceinline__ void vo_bucket_rank(ForEach for_each, uint32_t lo, ui
     const uint32_t end = word[b];
     uint32_t r = start;
     for (uint32_t t = start; t < end; ++t) r += comp[t] > c ? 1u : 0u;
-    out[r] = vo_column(c);
+    __builtin_nontemporal_store(vo_column(c), out + r);
   }
 }
 
