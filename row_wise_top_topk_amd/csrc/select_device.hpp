@@ -464,7 +464,10 @@ __device__ __forceinline__ Prefix rounds_window(const Src& src, uint32_t lo, uin
                                                 uint32_t need, int ib, uint32_t* hist,
                                                 uint32_t* res, uint32_t* wt,
                                                 bool hist_zero = false, bool equal_ok = false) {
-  int s = 0;
+  // the smallest shift s with (hi >> s) - (lo >> s) < 2^12: at least
+  // bitlen(hi - lo) - 12 (below it the difference is 2^12 or more), and at
+  // most one more than that (the difference falls as s grows)
+  int s = hi > lo ? max(0, 32 - __clz(hi - lo) - kFirstBits) : 0;
   while ((hi >> s) - (lo >> s) >= static_cast<uint32_t>(kFirstBins)) ++s;
   const uint32_t base = lo >> s;
   if (!hist_zero) {  // (uniform) else the caller cleared it before a barrier
