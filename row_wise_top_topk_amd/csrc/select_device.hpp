@@ -444,6 +444,16 @@ __device__ __forceinline__ Prefix finish_small(const Src& src, uint32_t kp, int 
   return Prefix{32 + ib, T, ((1u << ib) - 1u) - jt};
 }
 
+// The smallest shift s with (hi >> s) - (lo >> s) < kFirstBins (lo <= hi):
+// at least bitlen(hi - lo) - kFirstBits (below it the difference is
+// kFirstBins or more) and at most one more than that, since the difference
+// falls as s grows.
+__device__ __forceinline__ int window_shift(uint32_t lo, uint32_t hi) {
+  int s = hi > lo ? max(0, 32 - __clz(hi - lo) - kFirstBits) : 0;
+  while ((hi >> s) - (lo >> s) >= static_cast<uint32_t>(kFirstBins)) ++s;
+  return s;
+}
+
 // Radix rounds for entries whose keys all lie in [lo, hi] (entries outside
 // the row carry key 0).  The first round histograms the key bits just below
 // the ones every key in [lo, hi] shares: the shift s is the smallest that
@@ -464,11 +474,7 @@ __device__ __forceinline__ Prefix rounds_window(const Src& src, uint32_t lo, uin
                                                 uint32_t need, int ib, uint32_t* hist,
                                                 uint32_t* res, uint32_t* wt,
                                                 bool hist_zero = false, bool equal_ok = false) {
-  // the smallest shift s with (hi >> s) - (lo >> s) < 2^12: at least
-  // bitlen(hi - lo) - 12 (below it the difference is 2^12 or more), and at
-  // most one more than that (the difference falls as s grows)
-  int s = hi > lo ? max(0, 32 - __clz(hi - lo) - kFirstBits) : 0;
-  while ((hi >> s) - (lo >> s) >= static_cast<uint32_t>(kFirstBins)) ++s;
+  const int s = window_shift(lo, hi);
   const uint32_t base = lo >> s;
   if (!hist_zero) {  // (uniform) else the caller cleared it before a barrier
     for (int i = threadIdx.x; i < kFirstBins; i += BLOCK) hist[i] = 0;
@@ -604,8 +610,7 @@ struct VoBins {
     linear = lo >= kKeyNegInf && hi <= kKeyPosInf && __builtin_isfinite(xlo) && __builtin_isfinite(xhi) &&
              __builtin_isfinite(span) && span > 0.0f;
     scale = linear ? static_cast<float>(kFirstBins) / span : 0.0f;
-    s = 0;
-    while ((hi >> s) - (lo >> s) >= static_cast<uint32_t>(kFirstBins)) ++s;
+    s = window_shift(lo, hi);
     base = lo >> s;
   }
   __device__ __forceinline__ uint32_t operator()(uint32_t key) const {
