@@ -372,10 +372,15 @@ __device__ __forceinline__ void find_bucket_wave(const uint32_t* hist, int nb, u
 // from prefix p with `need` entries still to choose among p's bucket, the
 // prefix is refined one digit at a time until the bucket holding the need-th
 // entry contains exactly `need` entries.  Returns the final prefix: the
-// selected entries are those whose composite prefix is >= it.
+// selected entries are those whose composite prefix is >= it.  With
+// key_need, the rounds stop once the whole key T is known (32 bits) and its
+// bucket still holds more than the entries to take: *key_need is then set to
+// the number of entries equal to T to take (the first in column order, for
+// an emission that counts them), and the index digits are not visited.
 template <int BLOCK, class Src>
 __device__ __forceinline__ Prefix rounds_local(const Src& src, Prefix p, uint32_t need, int ib,
-                                               uint32_t* hist, uint32_t* res, uint32_t* wt) {
+                                               uint32_t* hist, uint32_t* res, uint32_t* wt,
+                                               uint32_t* key_need = nullptr) {
   const uint32_t rmask = (1u << ib) - 1u;
   for (int round = 0; round < kMaxRounds + 1; ++round) {
     const int d = digit_bits(p.bits, ib);
@@ -390,6 +395,10 @@ __device__ __forceinline__ Prefix rounds_local(const Src& src, Prefix p, uint32_
     need -= gt;
     p = extend(p, d, b);
     if (cnt == need) break;
+    if (key_need != nullptr && p.bits == 32) {
+      *key_need = need;
+      break;
+    }
   }
   return p;
 }

@@ -377,6 +377,33 @@ __device__ __forceinline__ void emit_regs(const uint32_t (&key)[E], const Chunk&
   }
 }
 
+// Ordered emission when the threshold key T is known but its ties are not
+// resolved by index digits: every entry with key above T, and of those equal
+// to T the first `ties` in column order, counted through the ballots (the
+// wavefronts' counts of both kinds packed in one word, each below 2^16).
+template <int BLOCK, int E>
+__device__ __forceinline__ void emit_ordered_ties(const uint32_t (&key)[E], const Chunk& ch, uint32_t T,
+                                                  uint32_t ties, const OutRow& out_row, uint32_t* wtot) {
+  static_assert(BLOCK * E < (1 << 16), "packed counts");
+  uint32_t n = 0;
+#pragma unroll
+  for (int u = 0; u < E; ++u) n += (key[u] > T ? 1u : 0u) + (key[u] == T ? 0x10000u : 0u);
+  const uint32_t off = wave_offset<BLOCK>(wave_sum(n), wtot);
+  uint32_t eq_seen = off >> 16;
+  uint32_t pos = (off & 0xFFFFu) + min(eq_seen, ties);
+  const int32_t j0 = ch.jbase + thread_elem0<E>();
+#pragma unroll
+  for (int u = 0; u < E; ++u) {
+    const bool eq = key[u] == T;
+    const uint64_t meq = __ballot(eq);
+    const bool sel = key[u] > T || (eq && eq_seen + lanes_below(meq) < ties);
+    const uint64_t m = __ballot(sel);
+    if (sel) out_row.put(pos + lanes_below(m), j0 + u * kWave);
+    pos += static_cast<uint32_t>(__popcll(m));
+    eq_seen += static_cast<uint32_t>(__popcll(meq));
+  }
+}
+
 template <int BLOCK, int E>
 __device__ __forceinline__ void emit_ordered(const uint32_t (&key)[E], const Chunk& ch,
                                              const Prefix& p, int ib, const OutRow& out_row,
@@ -1123,9 +1150,14 @@ __device__ __forceinline__ void select_chunk_whole_row(const uint32_t (&key)[E],
                                                        uint32_t* res) {
   const int ib = index_bits(L);
   const uint32_t kk = static_cast<uint32_t>(k);
-  const Prefix pf =
-      rounds_local<BLOCK>(RegSource<BLOCK, E>{key, ch}, Prefix{0, 0u, 0u}, kk, ib, hist, res, wtot);
-  emit_ordered<BLOCK, E>(key, ch, pf, ib, out_row, 0u, kk, wtot);
+  uint32_t ties = 0xFFFFFFFFu;  // set when the key is known and its ties are left to the emission
+  const Prefix pf = rounds_local<BLOCK>(RegSource<BLOCK, E>{key, ch}, Prefix{0, 0u, 0u}, kk, ib, hist, res,
+                                        wtot, &ties);
+  if (ties != 0xFFFFFFFFu) {
+    emit_ordered_ties<BLOCK, E>(key, ch, pf.kp, ties, out_row, wtot);
+  } else {
+    emit_ordered<BLOCK, E>(key, ch, pf, ib, out_row, 0u, kk, wtot);
+  }
 }
 
 // Two 512-thread workgroups per CU, so that up to 512 chunks are co-resident.
