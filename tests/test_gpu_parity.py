@@ -225,12 +225,15 @@ def test_chunks_long_workload_leaves_workspace_zero():
 
 @pytest.mark.parametrize("ties", [3, 10, 40, 200])
 @pytest.mark.parametrize("stride,k,path", [(32768, 2048, "auto"), (300032, 2048, "chunks"),
-                                           (60000, 1024, "chunks"), (20000, 512, "auto")])
+                                           (60000, 1024, "chunks"), (20000, 512, "auto"),
+                                           (16384, 1024, "chunks"), (9000, 512, "chunks")])
 def test_ties_straddle_the_threshold(stride, k, path, ties):
     # `ties` entries ranked around the k-th all take the k-th value, so the
     # threshold key is tied across the cut: the lowest columns among the
     # ties are selected.  Few ties stay inside a small last bucket (finished
-    # by one wavefront), many go through further radix rounds.
+    # by one wavefront), many go through further radix rounds; on the
+    # chunked path a row of one chunk (16384 entries or fewer) stops its
+    # rounds at the key and counts the ties in its emission.
     rows = 4
     rng = np.random.default_rng(stride * 7 + ties)
     x = rng.standard_normal((rows, stride)).astype(np.float32)
