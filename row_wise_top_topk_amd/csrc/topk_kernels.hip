@@ -1022,7 +1022,6 @@ __device__ __forceinline__ void stream_item(const Params& p, int64_t row) {
   // word loads need no 16-byte alignment, so the row starts at element 0
   const Chunk ch = make_chunk(row_ptr, 0, 0, 0, L);
   const int ib = index_bits(L);
-  const uint32_t rmask = (1u << ib) - 1u;
   const uint32_t kk = static_cast<uint32_t>(p.k);
   const int tid = threadIdx.x;
 
@@ -1767,6 +1766,24 @@ __device__ __forceinline__ void hist_add_entries(uint32_t* hist, BinOf bin_of, T
   }
 }
 
+// The J largest of v[0, N) in t, largest first (insertion: each value is
+// carried down the list, swapping with every smaller entry).
+template <int J, int N, int E>
+__device__ __forceinline__ void largest_of(const uint32_t (&v)[E], uint32_t (&t)[J]) {
+#pragma unroll
+  for (int j = 0; j < J; ++j) t[j] = 0u;
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    uint32_t x = v[u];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint32_t m = max(t[j], x);
+      x = min(t[j], x);
+      t[j] = m;
+    }
+  }
+}
+
 template <int BLOCK, int E, bool VO>
 __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
   constexpr int NW = BLOCK / kWave;
@@ -1860,20 +1877,41 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
   for (int v = 0; v < NW; ++v) ns += min(max(clen - v * kWave * E, 0), kWave * kChunkSamples);
   const uint32_t nd = ceil_mul_div(3u * kk, static_cast<uint32_t>(ns), 2u * static_cast<uint32_t>(L)) + 16u;
   // When nd is small against the 512 threads, each thread contributes only
-  // the largest of its samples: the nd largest samples then lie in nearly
-  // nd different threads, so the nd-th largest maximum is a bound just below
-  // the nd-th largest sample (never above it: the maxima are samples), found
-  // from 512 entries instead of 8192.  On smooth data the samples crowd into
-  // few first-digit bins, whose LDS atomics then serialise.
+  // the largest of its samples (nd <= 64), or its two (nd <= 256) or four
+  // (nd <= 1024) largest: the nd largest samples then lie in nearly nd
+  // different threads, or few threads hold more of them than they
+  // contribute, so the nd-th largest contribution is a bound just below the
+  // nd-th largest sample (never above it: contributions are samples), found
+  // from 512 to 2048 entries instead of 8192.  On smooth data the samples
+  // crowd into few first-digit bins, whose LDS atomics then serialise.
   const bool by_max = nd <= 64u;
+  const bool by_two = nd <= 256u;
+  const bool by_four = nd <= 1024u;
   uint32_t smax = 0;
+  uint32_t more[3] = {0u, 0u, 0u};  // (nd > 64) the next largest samples after smax
 #pragma unroll
   for (int u = 0; u < kChunkSamples; ++u) smax = max(smax, kv[u]);  // positions past the row: key 1
   for (int i = tid; i < kFirstBins; i += BLOCK) hist[i] = 0;
   if (tid == 0) res[0] = 0u;
   __syncthreads();
-  if (by_max) {
+  if (by_four) {
     if (smax > 1u) atomicAdd(&hist[smax >> (32 - kFirstBits)], 1u);
+    if (!by_max) {  // (uniform: these passes cost the nd <= 64 rows nothing)
+      if (by_two) {
+        uint32_t t[2];
+        largest_of<2, kChunkSamples>(kv, t);
+        more[0] = t[1];
+      } else {
+        uint32_t t[4];
+        largest_of<4, kChunkSamples>(kv, t);
+        more[0] = t[1];
+        more[1] = t[2];
+        more[2] = t[3];
+      }
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (more[j] > 1u) atomicAdd(&hist[more[j] >> (32 - kFirstBits)], 1u);
+    }
   } else {
     hist_add_entries<kChunkSamples>(
         hist, [&](int q) { return kv[q] >> (32 - kFirstBits); },
@@ -1893,9 +1931,15 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
     __syncthreads();  // res and hist are reused
     for (int i = tid; i < kNextBins; i += BLOCK) hist[i] = 0;
     __syncthreads();
-    if (by_max) {
+    if (by_four) {
       if ((smax >> (32 - kFirstBits)) == b0)
         atomicAdd(&hist[(smax >> (32 - kFirstBits - kNextBits)) & (kNextBins - 1)], 1u);
+      if (!by_max) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+          if ((more[j] >> (32 - kFirstBits)) == b0)
+            atomicAdd(&hist[(more[j] >> (32 - kFirstBits - kNextBits)) & (kNextBins - 1)], 1u);
+      }
     } else {
       hist_add_entries<kChunkSamples>(
           hist, [&](int q) { return (kv[q] >> (32 - kFirstBits - kNextBits)) & (kNextBins - 1); },

@@ -176,6 +176,23 @@ def test_chunks_long_rows(kind):
         assert np.array_equal(got, ref), f"{kind} {path}"
 
 
+@pytest.mark.parametrize("k", [1024, 2048])
+@pytest.mark.parametrize("kind", ["normal", "bf16", "ramp", "descending", "fineramp", "plateau"])
+def test_chunk_bound_tiers(kind, k):
+    # lengths that put a chunk's sample need nd = ceil(3 k n_s / 2L) + 16 in
+    # every tier of the sampled bound: each thread's largest sample
+    # (nd <= 64), its two largest (<= 256), its four largest (<= 1024), all
+    # of them; in ordered rows many of a chunk's largest samples share a
+    # thread, which lowers the bound of the first three
+    stride = 300032
+    lengths = [300000, 131072, 60000, 40000, 20000, 16385]
+    w = workloads.make_custom(len(lengths), stride, lengths, k, seed=29, kind=kind)
+    ref = expected(w)
+    for path in ("auto", "chunks"):
+        got = run_gpu(w, path=path)
+        assert np.array_equal(got, ref), f"{kind} k={k} {path}"
+
+
 def test_chunks_path_is_chosen_for_long_rows():
     plan = mt.plan_describe(8, 900096, 2048)
     assert plan["path"] == mt.PATH_CHUNKS
