@@ -2,7 +2,7 @@
 
 The SGLang PR #34167 page (实现拆解, item 4) validates its kernels with
 1500 random stress shapes, 500 CUDA-graph replays and a sweep over k.  Here:
-1500 random shapes (10 parts of 150), each run on the automatic path and on
+3000 random shapes (20 parts of 150), each run on the automatic path and on
 one forced path, and 500+ graph replays over fresh inputs on every kernel,
 every result compared element by element with the CPU oracle.  Each part
 stops at its first mismatch and names the case.
@@ -57,7 +57,7 @@ def _forced_path(rng, stride, k):
     return choices[int(rng.integers(0, len(choices)))]
 
 
-@pytest.mark.parametrize("part", range(10))
+@pytest.mark.parametrize("part", range(20))
 def test_random_matrix(part):
     rng = np.random.default_rng(10_000 + part)
     ws = None
