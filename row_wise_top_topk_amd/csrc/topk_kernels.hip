@@ -1799,8 +1799,14 @@ __device__ __forceinline__ void chunks_item(const Params& p, int64_t item) {
   __shared__ uint32_t res[13];
   const int tid = threadIdx.x;
   const int G = p.G;
-  const int64_t row = item / G;
-  const int g = static_cast<int>(item % G);
+  // Item i is chunk i / R of row i % R: the rows' chunks interleave in
+  // dispatch order, so each row has its share of the first workgroups to
+  // start (alone on their CU, their loads first in line) and of the later
+  // ones.  Row after row, the last rows' chunks all started second on their
+  // CU (long rows: those rows ended 3-4 us after the others), and a batch's
+  // later rows, whose selection may stream the row itself, started it late.
+  const int64_t row = item % p.num_rows;
+  const int g = static_cast<int>(item / p.num_rows);
   const int L = row_length(p, row);
   const OutRow out_row = out_row_of(p, row);
   const float* row_ptr = p.logits + row * p.row_stride;
